@@ -1,0 +1,254 @@
+"""Benchmark of the tiled BF16 attention hot path on one MI355X.
+
+One step = one full pass of the hot path on the Llama-2-7B attention shape
+(B=4, H=32, N=4096, d=128, causal, stabilised shift on): fa_fwd, then the
+backward's three kernels (row-dot prepass, dK/dV, dQ).  Inputs are resident in
+HBM before the timed region.  The step is timed as a whole (synchronised wall
+clock) and each kernel with HIP events on the stream it is launched on.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+
+Prints one JSON line.  FLOP are algorithmic: forward 4*B*H*N^2*d halved for
+causal; backward 2.5x the forward (five N^2 d products against two).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense BF16 MFMA
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+METRIC = "attn fwd/bwd TFLOP/s & % BF16 MFMA peak (1 GPU); max/mean |err| vs FP64 oracle"
+KERNEL_SOURCES = ["fa_device.hpp", "fa_fwd.hip", "fa_bwd.hip"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=48, help="heads the CPU oracle times")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for s in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "precision_numerics_fa_amd", "csrc", s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel: str):
+    """HBM bytes per launch for `kernel` from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != source_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the hot path needs no collectives; "
+              f"heads shard across GPUs with no communication). --gpus {args.gpus} is not run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fa_inputs as F
+    import precision_numerics_fa_amd as fa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    fa.load()
+
+    w = F.WORKLOADS["c4"].with_shape(with_do=True)
+    B, H, N, d = w.B, w.H, w.N, w.d
+    t0 = time.time()
+    full = F.full(w)
+    gen_s = time.time() - t0
+    dev = {n: torch.from_numpy(full[n].view(np.int16)).view(torch.bfloat16).cuda()
+           for n in ("q", "k", "v", "do")}
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dvec = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stab = True
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fwd(q, k, v, causal=True, stabilize=stab, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        fa.bwd_dot(o, do, dvec)
+        if ev is not None:
+            ev[2].record()
+        fa.bwd_dkdv(q, k, v, do, lse, dvec, causal=True, dk=dk, dv=dv)
+        if ev is not None:
+            ev[3].record()
+        fa.bwd_dq(q, k, v, do, lse, dvec, causal=True, dq=dq)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_step = wall * 1e3 / args.steps
+    names = ["fwd", "bwd_dot", "bwd_dkdv", "bwd_dq"]
+    kern_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events])) for i, n in enumerate(names)}
+
+    # stabilise off: forward only, for the cost of the fix
+    for _ in range(args.warmup):
+        fa.fwd(q, k, v, causal=True, stabilize=False, out=o, lse=lse)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        fa.fwd(q, k, v, causal=True, stabilize=False, out=o, lse=lse)
+    e1.record()
+    torch.cuda.synchronize()
+    fwd_off_ms = e0.elapsed_time(e1) / args.steps
+    fa.fwd(q, k, v, causal=True, stabilize=stab, out=o, lse=lse)  # restore the stabilised outputs
+    fa.bwd(q, k, v, o, do, lse, causal=True)
+    torch.cuda.synchronize()
+
+    fwd_flop = 4.0 * B * H * N * N * d / 2.0
+    bwd_flop = 2.5 * fwd_flop
+    step_flop = fwd_flop + bwd_flop
+    value = step_flop / (ms_step * 1e-3) / 1e12
+    # algorithmic FLOP attributed to each kernel: the dK/dV kernel carries four of
+    # the backward's five products (S, dP, dV, dK), the dQ kernel the fifth.
+    kflop = {"fwd": fwd_flop, "bwd_dot": 0.0, "bwd_dkdv": 0.8 * bwd_flop, "bwd_dq": 0.2 * bwd_flop}
+    elem = B * H * N * d
+    kbytes = {"fwd": 4 * elem * 2 + B * H * N * 4, "bwd_dot": 2 * elem * 2 + B * H * N * 4,
+              "bwd_dkdv": 6 * elem * 2 + 2 * B * H * N * 4, "bwd_dq": 5 * elem * 2 + 2 * B * H * N * 4}
+    kernel_names = {"fwd": "fwd_kernel", "bwd_dot": "bwd_dot_kernel", "bwd_dkdv": "bwd_dkdv_kernel",
+                    "bwd_dq": "bwd_dq_kernel"}
+    kernels = {}
+    for n in names:
+        t = kern_ms[n] * 1e-3
+        if kflop[n] > 0:
+            ach = kflop[n] / t / 1e12
+            kernels[n] = {"ms": round(kern_ms[n], 4), "bound": "mfma", "achieved": round(ach, 1),
+                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+        else:
+            ach = kbytes[n] / t / 1e9
+            kernels[n] = {"ms": round(kern_ms[n], 4), "bound": "hbm", "achieved": round(ach, 1),
+                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
+        kernels[n]["traffic"] = counter_traffic(kernel_names[n])
+    dominant = max(names, key=lambda n: kern_ms[n])
+    roofline = dict(kernels[dominant])
+    roofline.pop("ms")
+    roofline["kernel"] = kernel_names[dominant]
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama2-7b attention fwd+bwd, causal, stabilized (B=4 H=32 N=4096 d=128)",
+                   "B": B, "H": H, "N": N, "d": d, "causal": True, "stabilize": stab,
+                   "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(fwd_flop / (kern_ms["fwd"] * 1e-3) / 1e12, 1),
+        "fwd_pct_peak": round(100 * fwd_flop / (kern_ms["fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "bwd_tflops": round(bwd_flop / (sum(kern_ms[n] for n in names[1:]) * 1e-3) / 1e12, 1),
+        "fwd_stabilize_off_ms": round(fwd_off_ms, 4),
+        "fwd_stabilize_on_ms": round(kern_ms["fwd"], 4),
+        "kernels": kernels,
+        "roofline": roofline,
+        "input_gen_s": round(gen_s, 2),
+    }
+
+    if not args.no_cpu_baseline:
+        out.update(cpu_baseline_leg(w, full, o, lse, dq, dk, dv, args.cpu_heads, fwd_flop + bwd_flop))
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_leg(w, full, o, lse, dq, dk, dv, heads, step_flop):
+    """Time the float64 oracle on a few heads of the same workload, and check
+    the GPU's outputs for those heads against it."""
+    import platform
+
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import fa_inputs as F
+    from oracle import metrics as Mt
+    from oracle import reference as REF
+
+    pairs = F.sample_pairs(w, heads, seed=7)
+    f64 = lambda b: F.bf16_bits_to_f32(b).astype(np.float64)  # noqa: E731
+    t_cpu = 0.0
+    errs = {"max_abs": 0.0, "mean_abs": [], "max_rel_normwise": 0.0, "dq": 0.0, "dk": 0.0, "dv": 0.0,
+            "lse_max_abs": 0.0}
+    for (b, h) in pairs:
+        q, k, v, do = (f64(full[n][b, h]) for n in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        o_ref, lse_ref = REF.forward(q, k, v, w.scale, w.causal)
+        g_ref = REF.backward(q, k, v, do, w.scale, w.causal)
+        t_cpu += time.perf_counter() - t0
+        e = Mt.output_errors(o[b, h].float().cpu().numpy(), o_ref)
+        errs["max_abs"] = max(errs["max_abs"], e["max_abs"])
+        errs["mean_abs"].append(e["mean_abs"])
+        errs["max_rel_normwise"] = max(errs["max_rel_normwise"], e["max_rel_normwise"])
+        errs["lse_max_abs"] = max(errs["lse_max_abs"], float(np.abs(lse[b, h].cpu().numpy() - lse_ref).max()))
+        for n, g, r in (("dq", dq, g_ref[0]), ("dk", dk, g_ref[1]), ("dv", dv, g_ref[2])):
+            errs[n] = max(errs[n], Mt.relative_fro(g[b, h].float().cpu().numpy(), r))
+    errs["mean_abs"] = float(np.mean(errs["mean_abs"]))
+    per_head_flop = step_flop / (w.B * w.H)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    cpu_tflops = per_head_flop * len(pairs) / t_cpu / 1e12
+    return {
+        "cpu_baseline": {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": int(threads),
+                         "kind": "oracle",
+                         "sample": f"float64 oracle forward+backward on {len(pairs)} of {w.B * w.H} heads "
+                                   f"(N={w.N}, d={w.d}, causal), {t_cpu:.1f} s; TFLOP/s under the "
+                                   f"GPU's algorithmic FLOP count",
+                         "cpu": platform.processor() or platform.machine(), "seconds": round(t_cpu, 2)},
+        "accuracy": {"heads_checked": len(pairs), "o_max_abs": errs["max_abs"], "o_mean_abs": errs["mean_abs"],
+                     "o_max_rel_normwise": errs["max_rel_normwise"], "lse_max_abs": errs["lse_max_abs"],
+                     "dq_rel": errs["dq"], "dk_rel": errs["dk"], "dv_rel": errs["dv"]},
+    }
+
+
+if __name__ == "__main__":
+    main()

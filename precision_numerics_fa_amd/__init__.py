@@ -1,0 +1,30 @@
+"""Tiled BF16 FlashAttention forward/backward for AMD MI355X (gfx950).
+
+Thin Python binding of the C ABI in include/fa.h (libfa.so, built in-tree by
+``python -m precision_numerics_fa_amd.build``).  PyTorch supplies device
+memory and the current stream; every step of the computation runs in the HIP
+kernels.  There is no fallback: if the library is missing or the device is
+not a gfx950 GPU, the calls raise.
+
+    o, lse = fwd(q, k, v, causal=True, stabilize=True)
+    dq, dk, dv = bwd(q, k, v, o, do, lse, causal=True)
+
+Tensors are torch.bfloat16, shape (B, H, N, d), contiguous, on the current
+CUDA (HIP) device; LSE is float32 (B, H, N).
+"""
+from ._lib import (  # noqa: F401
+    FAError,
+    bwd,
+    bwd_dkdv,
+    bwd_dot,
+    bwd_dq,
+    fwd,
+    fwd_diag,
+    fwd_tile,
+    lib_path,
+    load,
+    stabilize_params,
+    status_string,
+    version,
+    workspace_bytes,
+)

@@ -1,0 +1,221 @@
+"""ctypes marshalling for libfa.so (argument checks and pointer passing only)."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libfa.so"
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_S = ctypes.c_size_t
+
+_SIGNATURES = {
+    "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_fwd_diag": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_dot": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
+    "fa_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
+    "fa_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
+    "fa_status_string": (ctypes.c_char_p, [_I]),
+    "fa_stabilize_params": (None, [ctypes.POINTER(_F)] * 3),
+    "fa_fwd_tile": (None, [_I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "fa_version": (_I, []),
+}
+
+
+class FAError(RuntimeError):
+    """A C ABI call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed with status {status}: {status_string(status)}")
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load():
+    """Load libfa.so (once) and declare the ABI signatures."""
+    global _lib
+    if _lib is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -m precision_numerics_fa_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(load().fa_version())
+
+
+def stabilize_params() -> Tuple[float, float, float]:
+    a, b, c = _F(), _F(), _F()
+    load().fa_stabilize_params(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    return a.value, b.value, c.value
+
+
+def fwd_tile(d: int) -> Tuple[int, int]:
+    q, k = _I(), _I()
+    load().fa_fwd_tile(int(d), ctypes.byref(q), ctypes.byref(k))
+    return q.value, k.value
+
+
+def workspace_bytes(B: int, H: int, N: int, d: int, causal: bool) -> int:
+    return int(load().fa_bwd_workspace_bytes(B, H, N, d, int(bool(causal))))
+
+
+# ---------------------------------------------------------------- tensor plumbing
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    torch = _torch()
+    return _P(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(name, t, dtype, shape, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _ptr(t):
+    return _P(t.data_ptr())
+
+
+def _call(fn: str, *args):
+    st = getattr(load(), fn)(*args)
+    if st != 0:
+        raise FAError(fn, st)
+
+
+def _shape(q):
+    if q.dim() != 4:
+        raise ValueError("q must have shape (B, H, N, d)")
+    return tuple(int(x) for x in q.shape)
+
+
+def _scale(scale: Optional[float], d: int) -> float:
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    return s
+
+
+def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None, stabilize: bool = False,
+        out=None, lse=None):
+    """Forward pass.  Returns (O bf16 (B,H,N,d), LSE fp32 (B,H,N))."""
+    torch = _torch()
+    B, H, N, d = _shape(q)
+    dev = q.device
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check(n, t, torch.bfloat16, (B, H, N, d), dev)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _check("out", o, torch.bfloat16, (B, H, N, d), dev)
+    _check("lse", l, torch.float32, (B, H, N), dev)
+    _call("fa_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, N, d, int(bool(causal)),
+          _scale(scale, d), int(bool(stabilize)), _stream())
+    return o, l
+
+
+def fwd_diag(q, k, v, causal: bool = False, scale: Optional[float] = None, stabilize: bool = False):
+    """Forward pass that also returns, per row, whether the stabilised shift
+    was applied at some key block (uint8 (B,H,N))."""
+    torch = _torch()
+    B, H, N, d = _shape(q)
+    dev = q.device
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check(n, t, torch.bfloat16, (B, H, N, d), dev)
+    o = torch.empty_like(q)
+    l = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    flags = torch.empty((B, H, N), dtype=torch.uint8, device=dev)
+    _call("fa_fwd_diag", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), _ptr(flags), B, H, N, d,
+          int(bool(causal)), _scale(scale, d), int(bool(stabilize)), _stream())
+    return o, l, flags
+
+
+def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
+        stabilize: bool = False, workspace=None):
+    """Backward pass.  Returns (dQ, dK, dV), bf16 (B,H,N,d)."""
+    torch = _torch()
+    B, H, N, d = _shape(q)
+    dev = q.device
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(n, t, torch.bfloat16, (B, H, N, d), dev)
+    _check("lse", lse, torch.float32, (B, H, N), dev)
+    nbytes = workspace_bytes(B, H, N, d, causal)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _call("fa_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+          _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, N, d, int(bool(causal)),
+          _scale(scale, d), int(bool(stabilize)), _stream())
+    return dq, dk, dv
+
+
+def bwd_dot(o, do, dvec=None):
+    """D = rowsum(dO * O) in fp32, (B,H,N)."""
+    torch = _torch()
+    B, H, N, d = _shape(o)
+    _check("do", do, torch.bfloat16, (B, H, N, d), o.device)
+    _check("o", o, torch.bfloat16, (B, H, N, d), o.device)
+    dvec = torch.empty((B, H, N), dtype=torch.float32, device=o.device) if dvec is None else dvec
+    _check("dvec", dvec, torch.float32, (B, H, N), o.device)
+    _call("fa_bwd_dot", _ptr(o), _ptr(do), _ptr(dvec), B, H, N, d, _stream())
+    return dvec
+
+
+def bwd_dkdv(q, k, v, do, lse, dvec, causal: bool = False, scale: Optional[float] = None, dk=None, dv=None):
+    torch = _torch()
+    B, H, N, d = _shape(q)
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for n, t in (("q", q), ("k", k), ("v", v), ("do", do), ("dk", dk), ("dv", dv)):
+        _check(n, t, torch.bfloat16, (B, H, N, d), q.device)
+    _check("lse", lse, torch.float32, (B, H, N), q.device)
+    _check("dvec", dvec, torch.float32, (B, H, N), q.device)
+    _call("fa_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dvec), _ptr(dk), _ptr(dv),
+          B, H, N, d, int(bool(causal)), _scale(scale, d), _stream())
+    return dk, dv
+
+
+def bwd_dq(q, k, v, do, lse, dvec, causal: bool = False, scale: Optional[float] = None, dq=None):
+    torch = _torch()
+    B, H, N, d = _shape(q)
+    dq = torch.empty_like(q) if dq is None else dq
+    for n, t in (("q", q), ("k", k), ("v", v), ("do", do), ("dq", dq)):
+        _check(n, t, torch.bfloat16, (B, H, N, d), q.device)
+    _check("lse", lse, torch.float32, (B, H, N), q.device)
+    _check("dvec", dvec, torch.float32, (B, H, N), q.device)
+    _call("fa_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dvec), _ptr(dq),
+          B, H, N, d, int(bool(causal)), _scale(scale, d), _stream())
+    return dq

@@ -1,0 +1,181 @@
+// C ABI of the attention library (declared in include/fa.h): argument
+// validation, device check, and dispatch to the kernel launchers.  Nothing
+// here allocates or keeps per-call state; the only cached state is a per-device
+// "is this a gfx950" flag, written with relaxed atomics (idempotent).
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "fa.h"
+#include "fa_device.hpp"
+#include "fa_launch.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA_ERR_DEVICE;
+  if (dev < kMaxDevices) {
+    const int known = g_device_ok[dev].load(std::memory_order_relaxed);
+    if (known != 0) return known > 0 ? FA_OK : FA_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FA_ERR_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_device_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+  return ok ? FA_OK : FA_ERR_DEVICE;
+}
+
+bool aligned(const void* p, size_t a) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const long double elems = (long double)B * H * N * d;
+  if (elems >= (long double)(1ULL << 40)) return FA_ERR_INVALID_ARG;
+  // grid sizes (B*H*ceil(N/64)) must fit a 32-bit launch dimension
+  if ((long double)B * H * ((N + 63) / 64) >= 2147483647.0L) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+int check_scale(float scale) { return (std::isfinite(scale) && scale > 0.0f) ? FA_OK : FA_ERR_INVALID_ARG; }
+
+int launched(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+int fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, unsigned char* flags,
+             int B, int H, int N, int d, int causal, float scale, int stabilize, void* stream) {
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 4))
+    return FA_ERR_INVALID_ARG;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if ((st = check_device()) != FA_OK) return st;
+  fa::FwdArgs a{Q, K, V, O, LSE, flags, B, H, N, d, causal != 0, stabilize != 0, scale};
+  (void)hipGetLastError();  // clear a stale error so a failure below is ours
+  return launched(fa::launch_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+int bwd_args(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+             const float* Dvec, int B, int H, int N, int d, float scale) {
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(dO, 16) || !aligned(LSE, 4) ||
+      !aligned(Dvec, 4))
+    return FA_ERR_INVALID_ARG;
+  return check_scale(scale);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N, int d,
+           int causal, float scale, int stabilize, void* stream) {
+  return fwd_impl(Q, K, V, O, LSE, nullptr, B, H, N, d, causal, scale, stabilize, stream);
+}
+
+int fa_fwd_diag(const void* Q, const void* K, const void* V, void* O, float* LSE, unsigned char* row_shifted,
+                int B, int H, int N, int d, int causal, float scale, int stabilize, void* stream) {
+  if (row_shifted == nullptr) return FA_ERR_INVALID_ARG;
+  return fwd_impl(Q, K, V, O, LSE, row_shifted, B, H, N, d, causal, scale, stabilize, stream);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int causal) {
+  (void)causal;
+  if (check_shape(B, H, N, d) != FA_OK) return 0;
+  const size_t bytes = (size_t)B * H * N * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int fa_bwd_dot(const void* O, const void* dO, float* Dvec, int B, int H, int N, int d, void* stream) {
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned(O, 16) || !aligned(dO, 16) || !aligned(Dvec, 4)) return FA_ERR_INVALID_ARG;
+  if ((st = check_device()) != FA_OK) return st;
+  fa::BwdArgs a{};
+  a.o = O;
+  a.dout = dO;
+  a.dvec = Dvec;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  (void)hipGetLastError();
+  return launched(fa::launch_bwd_dot(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                const float* Dvec, void* dK, void* dV, int B, int H, int N, int d, int causal, float scale,
+                void* stream) {
+  int st = bwd_args(Q, K, V, dO, LSE, Dvec, B, H, N, d, scale);
+  if (st != FA_OK) return st;
+  if (!aligned(dK, 16) || !aligned(dV, 16)) return FA_ERR_INVALID_ARG;
+  if ((st = check_device()) != FA_OK) return st;
+  fa::BwdArgs a{Q, K, V, nullptr, dO, LSE, const_cast<float*>(Dvec), nullptr, dK, dV, B, H, N, d, causal != 0, scale};
+  (void)hipGetLastError();
+  return launched(fa::launch_bwd_dkdv(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const float* LSE, const float* Dvec,
+              void* dQ, int B, int H, int N, int d, int causal, float scale, void* stream) {
+  int st = bwd_args(Q, K, V, dO, LSE, Dvec, B, H, N, d, scale);
+  if (st != FA_OK) return st;
+  if (!aligned(dQ, 16)) return FA_ERR_INVALID_ARG;
+  if ((st = check_device()) != FA_OK) return st;
+  fa::BwdArgs a{Q, K, V, nullptr, dO, LSE, const_cast<float*>(Dvec), dQ, nullptr, nullptr, B, H, N, d, causal != 0, scale};
+  (void)hipGetLastError();
+  return launched(fa::launch_bwd_dq(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
+           void* dK, void* dV, void* workspace, size_t workspace_bytes, int B, int H, int N, int d, int causal,
+           float scale, int stabilize, void* stream) {
+  (void)stabilize;  // the backward recomputes P from LSE; the shift has no influence on it
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(dO, 16) ||
+      !aligned(LSE, 4) || !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16))
+    return FA_ERR_INVALID_ARG;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (workspace == nullptr || !aligned(workspace, 4) || workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d, causal))
+    return FA_ERR_WORKSPACE;
+  if ((st = check_device()) != FA_OK) return st;
+  float* Dvec = static_cast<float*>(workspace);
+  fa::BwdArgs a{Q, K, V, O, dO, LSE, Dvec, dQ, dK, dV, B, H, N, d, causal != 0, scale};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if ((st = launched(fa::launch_bwd_dot(a, s))) != FA_OK) return st;
+  if ((st = launched(fa::launch_bwd_dkdv(a, s))) != FA_OK) return st;
+  return launched(fa::launch_bwd_dq(a, s));
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size, or bad scale)";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (d must be 64 or 128)";
+    case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_bwd_workspace_bytes()";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_DEVICE: return "current device is not a gfx950 GPU, or a device query failed";
+    default: return "unknown status";
+  }
+}
+
+void fa_stabilize_params(float* delta_min, float* delta_max, float* fold) {
+  if (delta_min) *delta_min = fa::kDeltaMin;
+  if (delta_max) *delta_max = fa::kDeltaMax;
+  if (fold) *fold = fa::kFold;
+}
+
+void fa_fwd_tile(int d, int* block_q, int* block_k) {
+  const bool ok = d == 64 || d == 128;
+  if (block_q) *block_q = ok ? fa::kFwdBlockQ : 0;
+  if (block_k) *block_k = ok ? fa::kFwdBlockK : 0;
+}
+
+int fa_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,405 @@
+// Tiled BF16 attention backward for gfx950 (MI355X), recomputing the
+// probabilities from the forward's LSE (so the stabilised shift, which only
+// changes the forward's intermediate scaling, plays no part here).
+//
+// Gradients of L = sum(O * dO) for softmax attention:
+//   D_i   = sum_t dO_it O_it               (bwd_dot, from the bf16 forward O)
+//   P_ij  = exp(S_ij - LSE_i)               (FP32, recomputed)
+//   dP_ij = dO_i . v_j
+//   dS_ij = P_ij (dP_ij - D_i)              (FP32, cast to bf16 for the products)
+//   dV_j  = sum_i bf16(P_ij) dO_i
+//   dK_j  = scale * sum_i bf16(dS_ij) q_i
+//   dQ_i  = scale * sum_j bf16(dS_ij) k_j
+// Page 1 (section 4.3) notes that gradients of Q and K inherit the forward's
+// errors through these quantities; the recipe itself is the standard one.
+//
+// Two compute kernels, no atomics, deterministic:
+//   bwd_dkdv: a workgroup owns 128 keys (32 per wave, kept in registers as
+//     B operands) and walks 64-query blocks of Q and dO staged in LDS.  It
+//     works in the S layout (rows = queries, lane = key), so P and dS are
+//     already B operands of dV^T = dO^T P and dK^T = Q^T dS, whose A
+//     operands dO^T and Q^T come from the row-major LDS tiles through the
+//     transposing LDS read.
+//   bwd_dq: a workgroup owns 128 queries (Q and dO rows in registers) and
+//     walks 64-key blocks of K and V in LDS.  It works in the S^T layout
+//     (lane = query), so dS^T is the B operand of dQ^T = K^T dS^T, whose A
+//     operand K^T is a transposing read of the K tile.
+// Scores and dP are recomputed in both (7 products instead of 5), which buys
+// determinism and no LDS round trip of P or dS.
+#include "fa_device.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+namespace {
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------- D = rowsum(dO * O)
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dot_kernel(const bf16_t* __restrict__ O,
+                                                      const bf16_t* __restrict__ dO,
+                                                      float* __restrict__ Dvec, long long rows) {
+  constexpr int TPR = D / 8;        // threads per row, one 16-byte chunk each
+  constexpr int RPB = 256 / TPR;    // rows per workgroup
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  float acc = 0.0f;
+  if (row < rows) {
+    const uint4 a = *reinterpret_cast<const uint4*>(O + row * D + c * 8);
+    const uint4 b = *reinterpret_cast<const uint4*>(dO + row * D + c * 8);
+    acc = bf16_lo(a.x) * bf16_lo(b.x) + bf16_hi(a.x) * bf16_hi(b.x) + bf16_lo(a.y) * bf16_lo(b.y) +
+          bf16_hi(a.y) * bf16_hi(b.y) + bf16_lo(a.z) * bf16_lo(b.z) + bf16_hi(a.z) * bf16_hi(b.z) +
+          bf16_lo(a.w) * bf16_lo(b.w) + bf16_hi(a.w) * bf16_hi(b.w);
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && c == 0) Dvec[row] = acc;
+}
+
+// ---------------------------------------------------------------- shared tiling
+template <int D>
+struct BwdTile {
+  static constexpr int B32 = 128;       // keys (dkdv) or queries (dq) per workgroup: 4 waves x 32
+  static constexpr int BS = 64;         // streamed rows per block
+  static constexpr int RS = D + 16;     // LDS row stride (elements), friendly to transposing reads
+  static constexpr int TILE = BS * RS;
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int CHUNKS = BS * D / 8 / 256;
+  static_assert(CHUNKS >= 1 && BS * D / 8 % 256 == 0, "tile/thread mismatch");
+};
+
+// Stage two row-major (BS x D) bf16 tiles, rows [r0, r0 + BS) of X and Y,
+// zero past N.
+template <int D>
+struct TilePair {
+  uint4 xr[BwdTile<D>::CHUNKS], yr[BwdTile<D>::CHUNKS];
+  __device__ __forceinline__ void load(const bf16_t* X, const bf16_t* Y, int r0, int N, int tid) {
+#pragma unroll
+    for (int r = 0; r < BwdTile<D>::CHUNKS; ++r) {
+      const int c = tid + 256 * r;
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      if (r0 + row < N) {
+        xr[r] = *reinterpret_cast<const uint4*>(X + (size_t)(r0 + row) * D + col);
+        yr[r] = *reinterpret_cast<const uint4*>(Y + (size_t)(r0 + row) * D + col);
+      } else {
+        xr[r] = make_uint4(0, 0, 0, 0);
+        yr[r] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* Xs, bf16_t* Ys, int tid) const {
+#pragma unroll
+    for (int r = 0; r < BwdTile<D>::CHUNKS; ++r) {
+      const int c = tid + 256 * r;
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(Xs + row * BwdTile<D>::RS + col) = xr[r];
+      *reinterpret_cast<uint4*>(Ys + row * BwdTile<D>::RS + col) = yr[r];
+    }
+  }
+};
+
+__device__ __forceinline__ void load_rows_as_b(bf16x8* f, const bf16_t* rowp, bool valid, int hi, int nsteps) {
+  for (int kk = 0; kk < nsteps; ++kk) {
+    if (valid) {
+      f[kk] = *reinterpret_cast<const bf16x8*>(rowp + kk * 16 + hi * 8);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[kk][j] = (__bf16)0.0f;
+    }
+  }
+}
+
+// Write a transposed 32x32 accumulator set (rows = d, lane = one output row)
+// as bf16: element i of subtile t is column d = 32 t + 8 (i/4) + 4 hi + i%4.
+template <int D>
+__device__ __forceinline__ void store_row_bf16(bf16_t* rowp, const f32x16* acc, float mul, int hi) {
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint2 w;
+      w.x = pack2(acc[t][4 * g + 0] * mul, acc[t][4 * g + 1] * mul);
+      w.y = pack2(acc[t][4 * g + 2] * mul, acc[t][4 * g + 3] * mul);
+      *reinterpret_cast<uint2*>(rowp + t * 32 + g * 8 + 4 * hi) = w;
+    }
+}
+
+// ---------------------------------------------------------------- dK, dV
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
+    bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int N, int n_kblk, int total_blocks,
+    int xcd_remap, float c2, float scale) {
+  using T = BwdTile<D>;
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * T::STAGE];
+  __shared__ float lse_s[2][T::BS];
+  __shared__ float dd_s[2][T::BS];
+
+  int bid = blockIdx.x;
+  if (xcd_remap) bid = (bid & 7) * (total_blocks >> 3) + (bid >> 3);
+  const int bh = bid / n_kblk;
+  const int kb = bid - bh * n_kblk;  // causal: the first key blocks carry the most work
+  const int k0 = kb * T::B32;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const size_t hoff = (size_t)bh * (size_t)N * D;
+  const bf16_t* Qh = Q + hoff;
+  const bf16_t* dOh = dO + hoff;
+  const float* LSEh = LSE + (size_t)bh * N;
+  const float* Dh = Dvec + (size_t)bh * N;
+
+  const int kw0 = k0 + wave * 32;
+  const int myk = kw0 + l32;
+  const bool wave_live = kw0 < N;
+
+  // This wave's K and V rows as B operands (n = key, k = d).
+  bf16x8 kf[D / 16], vf[D / 16];
+  load_rows_as_b(kf, K + hoff + (size_t)myk * D, myk < N, hi, D / 16);
+  load_rows_as_b(vf, V + hoff + (size_t)myk * D, myk < N, hi, D / 16);
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    dk[t] = zero16();
+    dv[t] = zero16();
+  }
+
+  const int q_first = CAUSAL ? k0 : 0;  // earlier queries see none of these keys
+  const int qb_first = q_first / T::BS;
+  const int qb_last = (N - 1) / T::BS;
+  const int g16 = lane >> 4, j16 = lane & 15, dsub = g16 & 1;
+
+  TilePair<D> pair;
+  float lse_r = 0.0f, dd_r = 0.0f;
+  auto gload = [&](int qb) {
+    pair.load(Qh, dOh, qb * T::BS, N, tid);
+    if (tid < T::BS) {
+      const int q = qb * T::BS + tid;
+      lse_r = q < N ? LSEh[q] * kLog2e : __builtin_huge_valf();  // P = 0 for rows past N
+      dd_r = q < N ? Dh[q] : 0.0f;
+    }
+  };
+  auto lstore = [&](int st) {
+    bf16_t* Qs = smem + st * T::STAGE;
+    pair.store(Qs, Qs + T::TILE, tid);
+    if (tid < T::BS) {
+      lse_s[st][tid] = lse_r;
+      dd_s[st][tid] = dd_r;
+    }
+  };
+
+  gload(qb_first);
+  lstore(0);
+  for (int qb = qb_first, it = 0; qb <= qb_last; ++qb, ++it) {
+    const int st = it & 1;
+    if (qb < qb_last) gload(qb + 1);
+    __syncthreads();
+    const bf16_t* Qs = smem + st * T::STAGE;
+    const bf16_t* dOs = Qs + T::TILE;
+
+    if (wave_live) {
+#pragma unroll
+      for (int qt = 0; qt < T::BS / 32; ++qt) {
+        const int qt0 = qb * T::BS + qt * 32;
+        if (CAUSAL && qt0 + 31 < kw0) continue;  // every query here precedes every key
+        f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const bf16x8 aq = lds_load8(Qs + (qt * 32 + l32) * T::RS + kk * 16 + hi * 8);
+          const bf16x8 ado = lds_load8(dOs + (qt * 32 + l32) * T::RS + kk * 16 + hi * 8);
+          s = mfma32x32x16(aq, kf[kk], s);
+          dp = mfma32x32x16(ado, vf[kk], dp);
+        }
+        // Entry i: query qt0 + 8 (i/4) + 4 hi + i%4, key myk.
+        const bool edge = CAUSAL && (qt0 < kw0 + 31);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ql = qt * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
+          float p = exp2_fast(__builtin_fmaf(s[i], c2, -lse_s[st][ql]));
+          if (edge && (qb * T::BS + ql < myk)) p = 0.0f;
+          s[i] = p;
+          dp[i] = p * (dp[i] - dd_s[st][ql]);
+        }
+        const bf16x8 pb0 = pack8(s, 0), pb1 = pack8(s, 8);
+        const bf16x8 sb0 = pack8(dp, 0), sb1 = pack8(dp, 8);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int row_lo = qt * 32 + ks * 16 + 4 * hi + (j16 >> 2);
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+            const int col = dt * 32 + 16 * dsub + 4 * (j16 & 3);
+            const bf16x8 a_do = join8(lds_load_tr4(dOs + row_lo * T::RS + col),
+                                      lds_load_tr4(dOs + (row_lo + 8) * T::RS + col));
+            const bf16x8 a_q = join8(lds_load_tr4(Qs + row_lo * T::RS + col),
+                                     lds_load_tr4(Qs + (row_lo + 8) * T::RS + col));
+            dv[dt] = mfma32x32x16(a_do, ks ? pb1 : pb0, dv[dt]);
+            dk[dt] = mfma32x32x16(a_q, ks ? sb1 : sb0, dk[dt]);
+          }
+        }
+      }
+    }
+    if (qb < qb_last) lstore(st ^ 1);
+  }
+
+  if (wave_live && myk < N) {
+    store_row_bf16<D>(dK + hoff + (size_t)myk * D, dk, scale, hi);
+    store_row_bf16<D>(dV + hoff + (size_t)myk * D, dv, 1.0f, hi);
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
+    bf16_t* __restrict__ dQ, int N, int n_qblk, int total_blocks, int xcd_remap, float c2,
+    float scale) {
+  using T = BwdTile<D>;
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * T::STAGE];
+
+  int bid = blockIdx.x;
+  if (xcd_remap) bid = (bid & 7) * (total_blocks >> 3) + (bid >> 3);
+  const int bh = bid / n_qblk;
+  const int qb = n_qblk - 1 - (bid - bh * n_qblk);
+  const int q0 = qb * T::B32;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const size_t hoff = (size_t)bh * (size_t)N * D;
+  const bf16_t* Kh = K + hoff;
+  const bf16_t* Vh = V + hoff;
+
+  const int qw0 = q0 + wave * 32;
+  const int myq = qw0 + l32;
+  const bool wave_live = qw0 < N;
+  const int wave_last_q = min(qw0 + 31, N - 1);
+
+  bf16x8 qf[D / 16], dof[D / 16];
+  load_rows_as_b(qf, Q + hoff + (size_t)myq * D, myq < N, hi, D / 16);
+  load_rows_as_b(dof, dO + hoff + (size_t)myq * D, myq < N, hi, D / 16);
+  const float lse2 = myq < N ? LSE[(size_t)bh * N + myq] * kLog2e : __builtin_huge_valf();
+  const float dq_d = myq < N ? Dvec[(size_t)bh * N + myq] : 0.0f;
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) dq[t] = zero16();
+
+  const int last_row = min(q0 + T::B32, N) - 1;
+  const int n_kblk = CAUSAL ? (last_row / T::BS + 1) : (N + T::BS - 1) / T::BS;
+  const int g16 = lane >> 4, j16 = lane & 15, dsub = g16 & 1;
+
+  TilePair<D> pair;
+  pair.load(Kh, Vh, 0, N, tid);
+  pair.store(smem, smem + T::TILE, tid);
+  for (int j = 0; j < n_kblk; ++j) {
+    if (j + 1 < n_kblk) pair.load(Kh, Vh, (j + 1) * T::BS, N, tid);
+    __syncthreads();
+    const bf16_t* Ks = smem + (j & 1) * T::STAGE;
+    const bf16_t* Vs = Ks + T::TILE;
+    const int kb0 = j * T::BS;
+
+    if (wave_live && (!CAUSAL || kb0 <= wave_last_q)) {
+      f32x16 s[T::BS / 32], dp[T::BS / 32];
+#pragma unroll
+      for (int t = 0; t < T::BS / 32; ++t) {
+        s[t] = zero16();
+        dp[t] = zero16();
+      }
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+#pragma unroll
+        for (int t = 0; t < T::BS / 32; ++t) {
+          const bf16x8 ak = lds_load8(Ks + (t * 32 + l32) * T::RS + kk * 16 + hi * 8);
+          const bf16x8 av = lds_load8(Vs + (t * 32 + l32) * T::RS + kk * 16 + hi * 8);
+          s[t] = mfma32x32x16(ak, qf[kk], s[t]);
+          dp[t] = mfma32x32x16(av, dof[kk], dp[t]);
+        }
+      }
+      // Entry (t, i): key kb0 + 32 t + 8 (i/4) + 4 hi + i%4, query myq.
+      const bool edge = (kb0 + T::BS > N) || (CAUSAL && kb0 + T::BS - 1 > qw0);
+#pragma unroll
+      for (int t = 0; t < T::BS / 32; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p = exp2_fast(__builtin_fmaf(s[t][i], c2, -lse2));
+          if (edge) {
+            const int key = kb0 + t * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
+            if (key >= N || (CAUSAL && key > myq)) p = 0.0f;
+          }
+          dp[t][i] = p * (dp[t][i] - dq_d);
+        }
+      bf16x8 sb[T::BS / 16];
+#pragma unroll
+      for (int ks = 0; ks < T::BS / 16; ++ks) sb[ks] = pack8(dp[ks >> 1], (ks & 1) * 8);
+#pragma unroll
+      for (int ks = 0; ks < T::BS / 16; ++ks) {
+        const int row_lo = ks * 16 + 4 * hi + (j16 >> 2);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const int col = dt * 32 + 16 * dsub + 4 * (j16 & 3);
+          const bf16x8 a_k = join8(lds_load_tr4(Ks + row_lo * T::RS + col),
+                                   lds_load_tr4(Ks + (row_lo + 8) * T::RS + col));
+          dq[dt] = mfma32x32x16(a_k, sb[ks], dq[dt]);
+        }
+      }
+    }
+    if (j + 1 < n_kblk) pair.store(smem + ((j + 1) & 1) * T::STAGE, smem + ((j + 1) & 1) * T::STAGE + T::TILE, tid);
+  }
+
+  if (wave_live && myq < N) store_row_bf16<D>(dQ + hoff + (size_t)myq * D, dq, scale, hi);
+}
+
+inline int remap_ok(long long total) { return (total % 8 == 0) ? 1 : 0; }
+
+template <int D>
+hipError_t launch_dot_t(const BwdArgs& a, hipStream_t s) {
+  const long long rows = (long long)a.B * a.H * a.N;
+  constexpr int RPB = 256 / (D / 8);
+  const long long blocks = (rows + RPB - 1) / RPB;
+  hipLaunchKernelGGL((bwd_dot_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, s, (const bf16_t*)a.o,
+                     (const bf16_t*)a.dout, a.dvec, rows);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
+  const int n_kblk = (a.N + BwdTile<D>::B32 - 1) / BwdTile<D>::B32;
+  const long long total = (long long)a.B * a.H * n_kblk;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)total), dim3(256), 0, s,
+                     (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.dout,
+                     a.lse, a.dvec, (bf16_t*)a.dk, (bf16_t*)a.dv, a.N, n_kblk, (int)total,
+                     remap_ok(total), scale_log2e(a.scale), a.scale);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
+  const int n_qblk = (a.N + BwdTile<D>::B32 - 1) / BwdTile<D>::B32;
+  const long long total = (long long)a.B * a.H * n_qblk;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)total), dim3(256), 0, s,
+                     (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.dout,
+                     a.lse, a.dvec, (bf16_t*)a.dq, a.N, n_qblk, (int)total, remap_ok(total),
+                     scale_log2e(a.scale), a.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dot(const BwdArgs& a, hipStream_t s) {
+  return a.d == 64 ? launch_dot_t<64>(a, s) : launch_dot_t<128>(a, s);
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s) {
+  if (a.d == 64) return a.causal ? launch_dkdv_t<64, true>(a, s) : launch_dkdv_t<64, false>(a, s);
+  return a.causal ? launch_dkdv_t<128, true>(a, s) : launch_dkdv_t<128, false>(a, s);
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s) {
+  if (a.d == 64) return a.causal ? launch_dq_t<64, true>(a, s) : launch_dq_t<64, false>(a, s);
+  return a.causal ? launch_dq_t<128, true>(a, s) : launch_dq_t<128, false>(a, s);
+}
+
+}  // namespace fa

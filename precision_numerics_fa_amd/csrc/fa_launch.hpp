@@ -1,0 +1,52 @@
+// Host-side launchers of the HIP kernels.  Arguments are assumed validated
+// by the C ABI layer (fa_api.hip); each launcher only sizes the grid and
+// enqueues on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  uint8_t* row_shifted;  // may be null (then no per-row report is written)
+  int B, H, N, d;
+  bool causal;
+  bool stabilize;
+  float scale;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* dvec;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, H, N, d;
+  bool causal;
+  float scale;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dot(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
+
+// scale * log2(e), rounded once to fp32 (the factor that folds the softmax
+// scale into the base-2 exponent).
+float scale_log2e(float scale);
+
+constexpr int kFwdBlockQ = 128;
+constexpr int kFwdBlockK = 64;
+
+}  // namespace fa

@@ -1,0 +1,95 @@
+"""The C-ABI library on the host: it loads, exports every function include/fa.h
+declares, validates arguments before touching any device, and refuses to run
+without a gfx950 GPU (no CPU fallback).  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import precision_numerics_fa_amd as fa
+from oracle import emulation as EMU
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = ctypes.c_void_p
+GOOD = P(4096)  # 16-byte aligned, never dereferenced on these paths
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "fa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.lib_path()):
+        pytest.fail("libfa.so is not built: run python -m precision_numerics_fa_amd.build")
+    return fa.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5, 7):
+        assert isinstance(fa.status_string(code), str) and fa.status_string(code)
+    assert fa.status_string(0) == "ok"
+
+
+def test_stabilize_constants_match_the_oracle(lib):
+    dmin, dmax, fold = fa.stabilize_params()
+    assert (dmin, dmax, fold) == (EMU.DELTA_MIN, EMU.DELTA_MAX, EMU.FOLD)
+
+
+def test_workspace_bytes(lib):
+    assert fa.workspace_bytes(4, 32, 4096, 128, True) == 4 * 32 * 4096 * 4
+    assert fa.workspace_bytes(1, 1, 3, 64, False) == 256
+    assert fa.workspace_bytes(1, 1, 0, 64, False) == 0
+    assert fa.workspace_bytes(1, 1, 8, 96, False) == 0
+
+
+def _fwd(lib, q=GOOD, k=GOOD, v=GOOD, o=GOOD, lse=GOOD, B=1, H=1, N=64, d=64, causal=0, scale=0.125,
+         stab=0):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stab, None)
+
+
+def test_forward_argument_validation(lib):
+    assert _fwd(lib, q=None) == -1
+    assert _fwd(lib, o=P(4100)) == -1          # misaligned output
+    assert _fwd(lib, lse=P(4098)) == -1        # misaligned LSE
+    assert _fwd(lib, N=0) == -1
+    assert _fwd(lib, B=-1) == -1
+    assert _fwd(lib, d=96) == -2
+    assert _fwd(lib, d=256) == -2
+    assert _fwd(lib, scale=0.0) == -1
+    assert _fwd(lib, scale=float("nan")) == -1
+    assert _fwd(lib, scale=float("inf")) == -1
+    assert _fwd(lib, B=1 << 20, H=1 << 10, N=1 << 12) == -1   # too many elements
+    assert lib.fa_fwd_diag(GOOD, GOOD, GOOD, GOOD, GOOD, None, 1, 1, 64, 64, 0, 0.125, 1, None) == -1
+
+
+def test_backward_argument_validation(lib):
+    args = [GOOD] * 9
+    need = fa.workspace_bytes(2, 2, 100, 64, True)
+    assert lib.fa_bwd(*args, None, need, 2, 2, 100, 64, 1, 0.125, 0, None) == -3
+    assert lib.fa_bwd(*args, GOOD, need - 4, 2, 2, 100, 64, 1, 0.125, 0, None) == -3
+    assert lib.fa_bwd(None, *args[1:], GOOD, need, 2, 2, 100, 64, 1, 0.125, 0, None) == -1
+    assert lib.fa_bwd(*args, GOOD, need, 2, 2, 100, 128 + 1, 1, 0.125, 0, None) == -2
+    assert lib.fa_bwd_dot(GOOD, None, GOOD, 1, 1, 8, 64, None) == -1
+    assert lib.fa_bwd_dkdv(*[GOOD] * 6, P(4097), GOOD, 1, 1, 8, 64, 1, 0.125, None) == -1
+    assert lib.fa_bwd_dq(*[GOOD] * 6, GOOD, 1, 1, 8, 64, 1, -1.0, None) == -1
+
+
+def test_no_gpu_means_an_error_not_a_fallback(lib):
+    """Valid arguments on a host without a gfx950 GPU: FA_ERR_DEVICE."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert _fwd(lib) == -5
+    need = fa.workspace_bytes(1, 1, 64, 64, False)
+    assert lib.fa_bwd(*[GOOD] * 9, GOOD, need, 1, 1, 64, 64, 0, 0.125, 0, None) == -5
