@@ -38,7 +38,21 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=48, help="heads the CPU oracle times")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB a few times "
+                         "(calibrates the HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def copy_probe(mib: int) -> None:
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n * 4, "launches": 5}), flush=True)
 
 
 def source_digest() -> str:
@@ -82,6 +96,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     fa.load()
 
     w = F.WORKLOADS["c4"].with_shape(with_do=True)
