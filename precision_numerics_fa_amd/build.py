@@ -49,6 +49,15 @@ def build(verbose: bool = False) -> str:
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln and ln.strip()]
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
+    # a kernel whose host-side launch stub was not emitted would only fail
+    # when the library is loaded; refuse such a build here
+    nm = shutil.which("nm")
+    if nm:
+        und = subprocess.run([nm, "-D", "--undefined-only", tmp], capture_output=True, text=True).stdout
+        missing = [ln.split()[-1] for ln in und.splitlines() if "__device_stub__" in ln]
+        if missing:
+            os.remove(tmp)
+            raise RuntimeError("hipcc produced a library with undefined kernel stubs: " + ", ".join(missing[:4]))
     os.replace(tmp, LIB)
     if verbose:
         print(" ".join(cmd))

@@ -85,15 +85,131 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int base) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// The repeated-maximum shift (base-2 units).  R = running max * scale*log2e.
-// Returns R + delta with delta = max(|R|, kDeltaMin), |R| folded by whole
-// multiples of kFold into (kDeltaMax - kFold, kDeltaMax] when larger than
-// kDeltaMax.  Every step is exact in fp32 except the final addition.
-__device__ __forceinline__ float shifted_offset(float R) {
-  float a = __builtin_fabsf(R);
-  if (a > kDeltaMax) a -= kFold * __builtin_ceilf((a - kDeltaMax) * (1.0f / kFold));
-  a = __builtin_fmaxf(a, kDeltaMin);
-  return R + a;
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wait until at most N vector-memory loads of this wave are outstanding
+// (loads retire in issue order, so the older ones have landed).
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// ---------------------------------------------------------------------------
+// Swizzled LDS tiles.  A tile holds ROWS rows of D bf16 with no padding; the
+// 16-byte chunk k of row r is stored at chunk position k ^ swz<D>(r).  LDS has
+// 64 four-byte banks, so a chunk position is a group of 4 banks and a D = 128
+// row spans all of them (a D = 64 row spans half; rows alternate halves).
+// The map is chosen so that both access patterns of the kernels are free of
+// bank conflicts:
+//   * 16 lanes reading the same logical chunk of 16 consecutive rows
+//     (ds_read_b128 of an MFMA operand with the row as m/n index);
+//   * 32 lanes of a transposing read: 4 consecutive rows (a multiple-of-4
+//     start) x 4 consecutive logical chunks starting at a multiple of 4.
+// D = 128: swz = 4 (r % 4) + (r / 4) % 4 -- the 16 rows get 16 distinct
+//   values, and 4 consecutive rows differ in bits 2-3, so an aligned block of
+//   4 chunks lands on 4 disjoint blocks.
+// D = 64: with u = (r / 2) % 8, swz = 4 (u % 2) + u / 2 -- a bijection of u
+//   for each row parity, and rows 4a, 4a+2 (same parity) differ in bit 2.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  const int u = (row >> 1) & 7;
+  return ((u & 1) << 2) | (u >> 1);
 }
+
+// Element offset of (row, col) in a swizzled tile.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int col) {
+  return row * D + ((((col >> 3) ^ swz<D>(row))) << 3) + (col & 7);
+}
+
+// Issue direct global -> LDS loads of rows [r0, r0 + ROWS) of a (N, D) bf16
+// matrix into a swizzled tile (NT threads; wave and lane as in the caller).
+// Rows past N read row N-1 (in bounds); zero_tail() clears them afterwards.
+template <int D, int ROWS, int NT>
+__device__ __forceinline__ void dma_tile(const bf16_t* __restrict__ X, int r0, int N, bf16_t* tile,
+                                         int wave, int lane) {
+  constexpr int CPR = D / 8;                 // chunks per row
+  constexpr int PER_LANE = ROWS * CPR / NT;
+  static_assert(PER_LANE >= 1 && ROWS * CPR % NT == 0, "tile/thread mismatch");
+#pragma unroll
+  for (int r = 0; r < PER_LANE; ++r) {
+    const int base = r * NT + wave * 64;     // wave-uniform first chunk of this load
+    const int c = base + lane;               // physical chunk written by this lane
+    const int row = c / CPR;
+    const int k = (c % CPR) ^ swz<D>(row);   // logical chunk stored at that position
+    const int src_row = min(r0 + row, N - 1);
+    __builtin_amdgcn_global_load_lds(X + (size_t)src_row * D + k * 8,
+                                     (__attribute__((address_space(3))) void*)(tile + base * 8), 16, 0, 0);
+  }
+}
+
+// Per-lane element offsets (within a ROWS x D block of the source matrix) of
+// the chunks dma_tile copies.  For a block that lies fully inside N the copy
+// is then a wave-uniform base pointer plus a fixed per-lane offset.
+template <int D, int ROWS, int NT>
+__device__ __forceinline__ void tile_offsets(int* off, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int PER_LANE = ROWS * CPR / NT;
+#pragma unroll
+  for (int r = 0; r < PER_LANE; ++r) {
+    const int c = r * NT + wave * 64 + lane;
+    const int row = c / CPR;
+    off[r] = row * D + (((c % CPR) ^ swz<D>(row)) << 3);
+  }
+}
+
+// Rows [r0, r0 + ROWS) of X (N rows) into a swizzled tile, using offsets
+// from tile_offsets(); a block crossing N takes the clamping path.
+template <int D, int ROWS, int NT>
+__device__ __forceinline__ void load_tile(const int* off, const bf16_t* __restrict__ X, int r0, int N,
+                                          bf16_t* tile, int wave, int lane) {
+  constexpr int PER_LANE = ROWS * (D / 8) / NT;
+  if (r0 + ROWS <= N) {
+    const bf16_t* base = X + (size_t)r0 * D;
+#pragma unroll
+    for (int r = 0; r < PER_LANE; ++r)
+      __builtin_amdgcn_global_load_lds(base + off[r],
+                                       (__attribute__((address_space(3))) void*)(tile + (r * NT + wave * 64) * 8),
+                                       16, 0, 0);
+  } else {
+    dma_tile<D, ROWS, NT>(X, r0, N, tile, wave, lane);
+  }
+}
+
+// Zero the rows of a swizzled tile that lie past N (after its loads landed).
+template <int D, int ROWS, int NT>
+__device__ __forceinline__ void zero_tail(int r0, int N, bf16_t* tile, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int PER_LANE = ROWS * CPR / NT;
+  if (r0 + ROWS <= N) return;
+#pragma unroll
+  for (int r = 0; r < PER_LANE; ++r) {
+    const int c = r * NT + wave * 64 + lane;
+    if (r0 + c / CPR >= N) *reinterpret_cast<uint4*>(tile + c * 8) = make_uint4(0, 0, 0, 0);
+  }
+}
+
+// The repeated-maximum shift (base-2 units).  R = running max * scale*log2e.
+// The shifted offset is R + delta with delta = max(|R|, kDeltaMin), |R|
+// folded by whole multiples of kFold into (kDeltaMax - kFold, kDeltaMax]
+// when larger than kDeltaMax.  Every step of delta is exact in fp32; delta is
+// finite for any R (a NaN from R = -inf is replaced by kDeltaMin).
+__device__ __forceinline__ float shift_delta(float R) {
+  const float a = __builtin_fabsf(R);
+  const float folded = a - kFold * __builtin_ceilf((a - kDeltaMax) * (1.0f / kFold));
+  const float d = a > kDeltaMax ? folded : a;
+  return __builtin_fmaxf(d, kDeltaMin);
+}
+
+// Offset for a row: R + delta when the running maximum is tied, else R.
+// Written as R + delta * {0, 1} (exactly R or R + delta) so that it stays
+// branch-free inside the softmax basic block.
+__device__ __forceinline__ float row_offset(float R, bool tied) {
+  return R + shift_delta(R) * (tied ? 1.0f : 0.0f);
+}
+
+// Scheduling-group masks for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedVALU = 0x002;
+constexpr int kSchedMFMA = 0x008;
+constexpr int kSchedDSRead = 0x100;
 
 }  // namespace fa

@@ -11,8 +11,9 @@
 // maximum is strictly below 1 (the rule is in fa_device.hpp).
 //
 // Mapping onto CDNA4.  A workgroup of 4 waves owns 128 query rows, 32 per
-// wave; keys arrive in blocks of 64, staged through LDS in two buffers (the
-// next block's global loads are in flight while the current one computes).
+// wave; keys arrive in blocks of 64.  K and V tiles are copied straight from
+// HBM into swizzled LDS tiles (global_load_lds_dwordx4, no register staging),
+// two blocks ahead for K and one ahead for V, with one barrier per block.
 // Scores are formed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16: K
 // rows come from LDS as the A operand, the wave's Q rows stay in registers as
 // the B operand, and each lane ends up owning one query row (lanes l and l+32
@@ -20,7 +21,9 @@
 // in-lane work plus one exchange with lane l^32, and the BF16 probabilities
 // are already laid out as the B operand of O^T = V^T P^T: no LDS round trip
 // for P.  V^T is read from the row-major V tile with the gfx950 transposing
-// LDS read.  O^T and l stay in registers until the epilogue.
+// LDS read.  O^T and l stay in registers until the epilogue.  The scores of
+// block j+1 are issued in the same basic block as the softmax of block j, so
+// the MFMAs of one overlap the VALU/exponential work of the other.
 //
 // Exponentials use exp2 with scale*log2(e) folded into one FMA:
 // P = 2^(t*c - M), t the raw FP32 dot product, c = scale*log2 e, M the shift
@@ -36,13 +39,16 @@ template <int D>
 struct FwdTile {
   static constexpr int BQ = kFwdBlockQ;  // query rows per workgroup (4 waves x 32)
   static constexpr int BK = kFwdBlockK;  // keys per block
-  static constexpr int KS = D + 8;       // LDS row stride of the K tile (elements)
-  static constexpr int VS = D + 16;      // LDS row stride of the V tile (transposing reads)
-  static constexpr int K_ELEMS = BK * KS;
-  static constexpr int V_ELEMS = BK * VS;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int CHUNKS = BK * D / 8 / 256;  // 16-byte chunks per thread per tensor
-  static_assert(CHUNKS >= 1 && BK * D / 8 % 256 == 0, "tile/thread mismatch");
+  static constexpr int TILE = BK * D;    // one swizzled K or V tile (elements)
+};
+
+// Per-wave softmax state of 32 query rows (one row per lane pair).
+struct RowState {
+  float m;     // running max of raw scores
+  float M;     // current shift, base-2 units
+  float l;     // partial row sum over this lane's keys
+  bool tied;   // running max attained at least twice
+  bool ever;   // the shift was applied at some block
 };
 
 template <int D, bool CAUSAL, bool STAB, bool DIAG>
@@ -51,7 +57,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
     bf16_t* __restrict__ O, float* __restrict__ LSE, uint8_t* __restrict__ row_shifted,
     int N, int n_qblk, int total_blocks, int xcd_remap, float c2) {
   using T = FwdTile<D>;
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * T::STAGE];
+  constexpr int NS = T::BK / 32;   // 32-key subtiles per block
+  constexpr int NK = T::BK / 16;   // 16-key MFMA steps per block
+  // two K tiles and two V tiles: K[j+1] and V[j] are read while K[j+2] and
+  // V[j+1] land (direct global -> LDS loads)
+  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * T::TILE];
+  bf16_t* const Kbuf = smem;
+  bf16_t* const Vbuf = smem + 2 * T::TILE;
 
   // Workgroup -> (head, query block).  The hardware hands workgroup i to XCD
   // i % 8; the remap gives each XCD a contiguous range of heads so that a
@@ -64,9 +76,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   const int q0 = qb * T::BQ;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  // wave index as a scalar: every per-wave condition below is then uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const size_t hoff = (size_t)bh * (size_t)N * D;
-  const bf16_t* Qh = Q + hoff;
   const bf16_t* Kh = K + hoff;
   const bf16_t* Vh = V + hoff;
 
@@ -75,165 +88,178 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   const bool wave_live = qw0 < N;
   const int wave_last_q = min(qw0 + 31, N - 1);
 
+  const int last_row = min(q0 + T::BQ, N) - 1;
+  const int n_kblk = CAUSAL ? (last_row / T::BK + 1) : (N + T::BK - 1) / T::BK;
+  // key blocks this wave computes (its causal bound), 0 for a wave past N
+  const int n_wave = !wave_live ? 0 : (CAUSAL ? min(n_kblk, wave_last_q / T::BK + 1) : n_kblk);
+
   // Q rows of this wave as B operands: element j of step kk is d = 16 kk + 8 hi + j.
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     if (myq < N) {
-      qf[kk] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)myq * D + kk * 16 + hi * 8);
+      qf[kk] = *reinterpret_cast<const bf16x8*>(Q + hoff + (size_t)myq * D + kk * 16 + hi * 8);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) qf[kk][j] = (__bf16)0.0f;
     }
   }
 
-  const int last_row = min(q0 + T::BQ, N) - 1;
-  const int n_kblk = CAUSAL ? (last_row / T::BK + 1) : (N + T::BK - 1) / T::BK;
-
-  // Global -> register -> LDS staging of one K block and one V block.
-  uint4 kr[T::CHUNKS], vr[T::CHUNKS];
-  auto gload = [&](int j) {
-    const int kb0 = j * T::BK;
+  // LDS offsets that do not change from block to block.
+  // K operand (row t*32 + l32, chunk 2 kk + hi): swz depends on l32 only.
+  int koff[D / 16];
 #pragma unroll
-    for (int r = 0; r < T::CHUNKS; ++r) {
-      const int c = tid + 256 * r;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int key = kb0 + row;
-      if (key < N) {
-        kr[r] = *reinterpret_cast<const uint4*>(Kh + (size_t)key * D + col);
-        vr[r] = *reinterpret_cast<const uint4*>(Vh + (size_t)key * D + col);
-      } else {
-        kr[r] = make_uint4(0, 0, 0, 0);  // zero keys/values past N: masked scores
-        vr[r] = make_uint4(0, 0, 0, 0);  // get probability 0, and 0 * 0 stays 0
-      }
-    }
-  };
-  auto lstore = [&](int st) {
-    bf16_t* Ks = smem + st * T::STAGE;
-    bf16_t* Vs = Ks + T::K_ELEMS;
+  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = tile_off<D>(l32, kk * 16 + hi * 8);
+  // V^T operand by transposing reads: row ks*16 + 8 r + 4 hi + j16/4,
+  // column dt*32 + 16 dsub + 4 (j16 % 4); swz does not depend on ks.
+  const int j16 = lane & 15, dsub = (lane >> 4) & 1;
+  int voff[2][D / 32];
 #pragma unroll
-    for (int r = 0; r < T::CHUNKS; ++r) {
-      const int c = tid + 256 * r;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(Ks + row * T::KS + col) = kr[r];
-      *reinterpret_cast<uint4*>(Vs + row * T::VS + col) = vr[r];
-    }
-  };
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+      voff[r][dt] = tile_off<D>(8 * r + 4 * hi + (j16 >> 2), dt * 32 + 16 * dsub + 4 * (j16 & 3));
 
-  // Running row state (both lanes of a row hold the same m, M, tie flag;
-  // each keeps the partial sum of its own half of the keys).
-  float m = kNegInf;   // running max of raw scores
-  float M = kNegInf;   // current shift, base-2 units
-  float l = 0.0f;      // partial row sum of this lane's probabilities
-  bool tied = false;   // running max attained at least twice
-  bool ever = false;   // the shift was applied at some block
+  int ldoff[T::BK * D / 8 / 256];
+  tile_offsets<D, T::BK, 256>(ldoff, wave, lane);
+
+  RowState st{kNegInf, kNegInf, 0.0f, false, false};
   f32x16 o[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) o[t] = zero16();
 
-  const int g16 = lane >> 4, j16 = lane & 15;
-  const int dsub = g16 & 1;  // lanes 16..31 and 48..63 read d + 16 in the V^T operand
+  // S^T = K Q^T for one block, raw FP32 dot products.
+  auto scores = [&](const bf16_t* Ks, f32x16* s) {
+#pragma unroll
+    for (int t = 0; t < NS; ++t) s[t] = zero16();
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+        s[t] = mfma32x32x16(lds_load8(Ks + t * 32 * D + koff[kk]), qf[kk], s[t]);
+  };
 
-  gload(0);
-  lstore(0);
-  for (int j = 0; j < n_kblk; ++j) {
-    if (j + 1 < n_kblk) gload(j + 1);
-    __syncthreads();
-    const bf16_t* Ks = smem + (j & 1) * T::STAGE;
-    const bf16_t* Vs = Ks + T::K_ELEMS;
-    const int kb0 = j * T::BK;
-
-    if (wave_live && (!CAUSAL || kb0 <= wave_last_q)) {
-      // ---- S^T = K Q^T: two 32-key subtiles, raw FP32 dot products
-      f32x16 s[T::BK / 32];
+  // Online softmax of one block held in s (masked already): updates the row
+  // state, rescales O, and returns bf16(P) as B operands in pb.
+  auto softmax = [&](f32x16* s, bf16x8* pb) {
+    // block row maximum; stabilised: also the second largest value, two
+    // entries at a time: a' = max(a, x, y), b' = max(b, med3(a, x, y))
+    float mx = kNegInf, m2 = kNegInf;
 #pragma unroll
-      for (int t = 0; t < T::BK / 32; ++t) s[t] = zero16();
+    for (int t = 0; t < NS; ++t)
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-#pragma unroll
-        for (int t = 0; t < T::BK / 32; ++t) {
-          const bf16x8 a = lds_load8(Ks + (t * 32 + l32) * T::KS + kk * 16 + hi * 8);
-          s[t] = mfma32x32x16(a, qf[kk], s[t]);
-        }
+      for (int i = 0; i < 16; i += 2) {
+        const float x = s[t][i], y = s[t][i + 1];
+        if (STAB) m2 = __builtin_fmaxf(m2, __builtin_amdgcn_fmed3f(mx, x, y));
+        mx = __builtin_fmaxf(mx, __builtin_fmaxf(x, y));
       }
-      // ---- mask keys past N and, on the diagonal, keys after the query
-      const bool edge = (kb0 + T::BK > N) || (CAUSAL && kb0 + T::BK - 1 > qw0);
-      if (edge) {
-#pragma unroll
-        for (int t = 0; t < T::BK / 32; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kb0 + t * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
-            if (key >= N || (CAUSAL && key > myq)) s[t][i] = kNegInf;
-          }
-      }
-      // ---- block row maximum (and, stabilised, the second largest value)
-      float mx = kNegInf, m2 = kNegInf;
-#pragma unroll
-      for (int t = 0; t < T::BK / 32; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (STAB) m2 = __builtin_amdgcn_fmed3f(mx, m2, s[t][i]);
-          mx = __builtin_fmaxf(mx, s[t][i]);
-        }
-      const float omx = __shfl_xor(mx, 32);
-      const float bm = __builtin_fmaxf(mx, omx);
-      if (STAB) {
-        const float om2 = __shfl_xor(m2, 32);
-        const float b2 = __builtin_fmaxf(__builtin_fminf(mx, omx), __builtin_fmaxf(m2, om2));
-        const bool btie = (b2 == bm) && (bm > kNegInf);
-        // Running count >= 2: a new maximum restarts the count with this
-        // block's; an equal maximum adds to it; a smaller one leaves it.
-        tied = (bm > m) ? btie : ((bm == m && bm > kNegInf) ? true : tied);
-      }
-      const float m_new = __builtin_fmaxf(m, bm);
-      const float R = m_new * c2;
-      float Mn = R;
-      if (STAB && tied) {
-        Mn = shifted_offset(R);
-        if (DIAG) ever = true;
-      }
-      const float alpha = exp2_fast(M - Mn);  // 0 on the first block (M = -inf)
-      M = Mn;
-      m = m_new;
-
-      // ---- P = 2^(t c - M); partial row sum
-      float lsum = 0.0f;
-#pragma unroll
-      for (int t = 0; t < T::BK / 32; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = exp2_fast(__builtin_fmaf(s[t][i], c2, -M));
-          s[t][i] = p;
-          lsum += p;
-        }
-      l = alpha * l + lsum;
-
-      // ---- O^T = alpha O^T + V^T bf16(P)^T
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
-      bf16x8 pb[T::BK / 16];
-#pragma unroll
-      for (int ks = 0; ks < T::BK / 16; ++ks) pb[ks] = pack8(s[ks >> 1], (ks & 1) * 8);
-#pragma unroll
-      for (int ks = 0; ks < T::BK / 16; ++ks) {
-        const int row_lo = ks * 16 + 4 * hi + (j16 >> 2);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const int col = dt * 32 + 16 * dsub + 4 * (j16 & 3);
-          const s16x4 lo = lds_load_tr4(Vs + row_lo * T::VS + col);
-          const s16x4 up = lds_load_tr4(Vs + (row_lo + 8) * T::VS + col);
-          o[dt] = mfma32x32x16(join8(lo, up), pb[ks], o[dt]);
-        }
-      }
+    const float omx = __shfl_xor(mx, 32);
+    const float bm = __builtin_fmaxf(mx, omx);
+    if (STAB) {
+      const float om2 = __shfl_xor(m2, 32);
+      const float b2 = __builtin_fmaxf(__builtin_fminf(mx, omx), __builtin_fmaxf(m2, om2));
+      const bool btie = (b2 == bm) && (bm > kNegInf);
+      // Running count >= 2: a new maximum restarts the count with this
+      // block's; an equal maximum adds to it; a smaller one leaves it.
+      st.tied = (bm > st.m) ? btie : ((bm == st.m && bm > kNegInf) ? true : st.tied);
     }
-    if (j + 1 < n_kblk) lstore((j + 1) & 1);
+    const float m_new = __builtin_fmaxf(st.m, bm);
+    const float R = m_new * c2;
+    float Mn = R;
+    if (STAB) {
+      Mn = row_offset(R, st.tied);
+      if (DIAG) st.ever = st.ever || st.tied;
+    }
+    const float alpha = exp2_fast(st.M - Mn);  // 0 on the first block (M = -inf)
+    st.M = Mn;
+    st.m = m_new;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NS; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = exp2_fast(__builtin_fmaf(s[t][i], c2, -Mn));
+        s[t][i] = p;
+        lsum += p;
+      }
+    st.l = alpha * st.l + lsum;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) pb[ks] = pack8(s[ks >> 1], (ks & 1) * 8);
+  };
+
+  // O^T += V^T bf16(P)^T for one block.
+  auto pv = [&](const bf16_t* Vs, const bf16x8* pb) {
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const bf16_t* base = Vs + ks * 16 * D;
+        const bf16x8 a = join8(lds_load_tr4(base + voff[0][dt]), lds_load_tr4(base + voff[1][dt]));
+        o[dt] = mfma32x32x16(a, pb[ks], o[dt]);
+      }
+  };
+
+  auto mask = [&](f32x16* s, int kb0) {
+#pragma unroll
+    for (int t = 0; t < NS; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb0 + t * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
+        if (key >= N || (CAUSAL && key > myq)) s[t][i] = kNegInf;
+      }
+  };
+
+  // ---- prologue: K0, V0 (and K1) into LDS; scores of block 0
+  load_tile<D, T::BK, 256>(ldoff, Kh, 0, N, Kbuf, wave, lane);
+  load_tile<D, T::BK, 256>(ldoff, Vh, 0, N, Vbuf, wave, lane);
+  if (n_kblk > 1) load_tile<D, T::BK, 256>(ldoff, Kh, T::BK, N, Kbuf + T::TILE, wave, lane);
+  wait_vmem();
+  zero_tail<D, T::BK, 256>(0, N, Kbuf, wave, lane);
+  zero_tail<D, T::BK, 256>(0, N, Vbuf, wave, lane);
+  if (n_kblk > 1) zero_tail<D, T::BK, 256>(T::BK, N, Kbuf + T::TILE, wave, lane);
+  __syncthreads();
+
+  // Two score buffers swap roles every block (the loop is unrolled by two),
+  // so the next block's scores need no register copy.
+  f32x16 sa[NS], sb[NS];
+  if (n_wave > 0) scores(Kbuf, sa);
+
+  auto iteration = [&](int j, f32x16* sc, f32x16* sn) {
+    // Prefetch: K[j+2] into the K tile block j used, V[j+1] into the V tile
+    // block j-1 used; both were released by the barrier that ended j-1.
+    bf16_t* const kdst = Kbuf + (j & 1) * T::TILE;
+    bf16_t* const vdst = Vbuf + ((j + 1) & 1) * T::TILE;
+    if (j + 2 < n_kblk) load_tile<D, T::BK, 256>(ldoff, Kh, (j + 2) * T::BK, N, kdst, wave, lane);
+    if (j + 1 < n_kblk) load_tile<D, T::BK, 256>(ldoff, Vh, (j + 1) * T::BK, N, vdst, wave, lane);
+
+    if (j < n_wave) {
+      const int kb0 = j * T::BK;
+      if ((kb0 + T::BK > N) || (CAUSAL && kb0 + T::BK - 1 > qw0)) mask(sc, kb0);
+      // The scores of the next block are issued together with this block's
+      // softmax: independent work in one basic block, so the MFMAs can
+      // overlap the VALU and exponential instructions.  On the wave's last
+      // block they read a stale (in-bounds) tile and are discarded.
+      bf16x8 pb[NK];
+      scores(Kbuf + ((j + 1) & 1) * T::TILE, sn);
+      softmax(sc, pb);
+      pv(Vbuf + (j & 1) * T::TILE, pb);
+    }
+    wait_vmem();
+    if (j + 2 < n_kblk) zero_tail<D, T::BK, 256>((j + 2) * T::BK, N, kdst, wave, lane);
+    if (j + 1 < n_kblk) zero_tail<D, T::BK, 256>((j + 1) * T::BK, N, vdst, wave, lane);
+    __syncthreads();
+  };
+  for (int j = 0; j < n_kblk; j += 2) {
+    iteration(j, sa, sb);
+    if (j + 1 < n_kblk) iteration(j + 1, sb, sa);
   }
 
   // ---- epilogue: O = O_bar / l (as O_bar * (1/l)), LSE = (M + log2 l) ln 2
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = st.l + __shfl_xor(st.l, 32);
   if (wave_live && myq < N) {
     const float rinv = 1.0f / lt;
     bf16_t* Orow = O + hoff + (size_t)myq * D;
@@ -247,8 +273,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
         *reinterpret_cast<uint2*>(Orow + t * 32 + g * 8 + 4 * hi) = w;
       }
     if (hi == 0) {
-      LSE[(size_t)bh * N + myq] = (M + __builtin_log2f(lt)) * kLn2;
-      if (DIAG) row_shifted[(size_t)bh * N + myq] = ever ? 1 : 0;
+      LSE[(size_t)bh * N + myq] = (st.M + __builtin_log2f(lt)) * kLn2;
+      if (DIAG) row_shifted[(size_t)bh * N + myq] = st.ever ? 1 : 0;
     }
   }
 }
