@@ -25,7 +25,9 @@
 //     (lane = query), so dS^T is the B operand of dQ^T = K^T dS^T, whose A
 //     operand K^T is a transposing read of the K tile.
 // Scores and dP are recomputed in both (7 products instead of 5), which buys
-// determinism and no LDS round trip of P or dS.
+// determinism and no LDS round trip of P or dS.  The dQ kernel reads K and V
+// from swizzled tiles copied straight into LDS and overlaps the second key
+// subtile's S/dP products with the first subtile's elementwise work.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -58,10 +60,13 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const bf16_t* __restrict__
 }
 
 // ---------------------------------------------------------------- shared tiling
+// dK/dV kernel tiling: row-major tiles staged through registers with a
+// padded row stride (its simple addressing keeps the kernel's register
+// footprint within one wave per SIMD without extra accumulator moves).
 template <int D>
-struct BwdTile {
-  static constexpr int B32 = 128;       // keys (dkdv) or queries (dq) per workgroup: 4 waves x 32
-  static constexpr int BS = 64;         // streamed rows per block
+struct DkdvTile {
+  static constexpr int B32 = 128;       // keys per workgroup: 4 waves x 32
+  static constexpr int BS = 64;         // query rows per block
   static constexpr int RS = D + 16;     // LDS row stride (elements), friendly to transposing reads
   static constexpr int TILE = BS * RS;
   static constexpr int STAGE = 2 * TILE;
@@ -73,10 +78,10 @@ struct BwdTile {
 // zero past N.
 template <int D>
 struct TilePair {
-  uint4 xr[BwdTile<D>::CHUNKS], yr[BwdTile<D>::CHUNKS];
+  uint4 xr[DkdvTile<D>::CHUNKS], yr[DkdvTile<D>::CHUNKS];
   __device__ __forceinline__ void load(const bf16_t* X, const bf16_t* Y, int r0, int N, int tid) {
 #pragma unroll
-    for (int r = 0; r < BwdTile<D>::CHUNKS; ++r) {
+    for (int r = 0; r < DkdvTile<D>::CHUNKS; ++r) {
       const int c = tid + 256 * r;
       const int row = c / (D / 8), col = (c % (D / 8)) * 8;
       if (r0 + row < N) {
@@ -90,11 +95,11 @@ struct TilePair {
   }
   __device__ __forceinline__ void store(bf16_t* Xs, bf16_t* Ys, int tid) const {
 #pragma unroll
-    for (int r = 0; r < BwdTile<D>::CHUNKS; ++r) {
+    for (int r = 0; r < DkdvTile<D>::CHUNKS; ++r) {
       const int c = tid + 256 * r;
       const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(Xs + row * BwdTile<D>::RS + col) = xr[r];
-      *reinterpret_cast<uint4*>(Ys + row * BwdTile<D>::RS + col) = yr[r];
+      *reinterpret_cast<uint4*>(Xs + row * DkdvTile<D>::RS + col) = xr[r];
+      *reinterpret_cast<uint4*>(Ys + row * DkdvTile<D>::RS + col) = yr[r];
     }
   }
 };
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
     bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int N, int n_kblk, int total_blocks,
     int xcd_remap, float c2, float scale) {
-  using T = BwdTile<D>;
+  using T = DkdvTile<D>;
   __shared__ __attribute__((aligned(16))) bf16_t smem[2 * T::STAGE];
   __shared__ float lse_s[2][T::BS];
   __shared__ float dd_s[2][T::BS];
@@ -144,7 +149,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int k0 = kb * T::B32;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const size_t hoff = (size_t)bh * (size_t)N * D;
   const bf16_t* Qh = Q + hoff;
   const bf16_t* dOh = dO + hoff;
@@ -250,15 +256,62 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   }
 }
 
+// dQ kernel tiling: swizzled tiles loaded straight into LDS.
+template <int D>
+struct DqTile {
+  static constexpr int B32 = 128;          // queries per workgroup: 4 waves x 32
+  static constexpr int BS = 64;            // keys per block (two 32-key subtiles)
+  static constexpr int TILE = BS * D;      // one swizzled tile (elements)
+  static constexpr int NT = 256;
+  static constexpr int PER = BS * D / 8 / NT;  // 16-byte loads per lane per tile
+};
+
+// Lane constants for reading a swizzled (64 x D) tile: the row-major operand
+// read (row sub*32 + l32, chunk 2 kk + hi) and the transposing read (row
+// sub*32 + ks*16 + 8 r + 4 hi + j16/4, column dt*32 + 16 dsub + 4 (j16 % 4)).
+// The swizzle depends only on the row modulo 16.
+template <int D>
+struct TileReader {
+  int rsw;                 // swizzle of the row-major operand row
+  int trow, tsw0, tsw1;    // transposing read: first row, swizzles of rows trow and trow + 8
+  int tcol;                // transposing read: column within a 32-wide d tile
+  int l32, hi;
+  __device__ __forceinline__ bf16x8 row8(const bf16_t* tile, int sub, int kk) const {
+    return lds_load8(tile + (sub * 32 + l32) * D + (((2 * kk + hi) ^ rsw) << 3));
+  }
+  // 8 bf16 of column (dt*32 + lane's d) for the 16 rows sub*32 + ks*16 + (0..15)
+  __device__ __forceinline__ bf16x8 col8(const bf16_t* tile, int sub, int ks, int dt) const {
+    const bf16_t* base = tile + (sub * 32 + ks * 16) * D;
+    const int c = dt * 32 + tcol;
+    return join8(lds_load_tr4(base + trow * D + (((c >> 3) ^ tsw0) << 3) + (c & 7)),
+                 lds_load_tr4(base + (trow + 8) * D + (((c >> 3) ^ tsw1) << 3) + (c & 7)));
+  }
+};
+
+template <int D>
+__device__ __forceinline__ TileReader<D> make_reader(int lane) {
+  TileReader<D> r;
+  r.l32 = lane & 31;
+  r.hi = lane >> 5;
+  r.rsw = swz<D>(r.l32);
+  const int j16 = lane & 15, dsub = (lane >> 4) & 1;
+  r.trow = 4 * r.hi + (j16 >> 2);
+  r.tsw0 = swz<D>(r.trow);
+  r.tsw1 = swz<D>(r.trow + 8);
+  r.tcol = 16 * dsub + 4 * (j16 & 3);
+  return r;
+}
+
 // ---------------------------------------------------------------- dQ
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
     bf16_t* __restrict__ dQ, int N, int n_qblk, int total_blocks, int xcd_remap, float c2,
     float scale) {
-  using T = BwdTile<D>;
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * T::STAGE];
+  using T = DqTile<D>;
+  // ring of two (K tile, V tile) pairs
+  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * T::TILE];
 
   int bid = blockIdx.x;
   if (xcd_remap) bid = (bid & 7) * (total_blocks >> 3) + (bid >> 3);
@@ -267,13 +320,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(
   const int q0 = qb * T::B32;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hi = lane >> 5;
   const size_t hoff = (size_t)bh * (size_t)N * D;
   const bf16_t* Kh = K + hoff;
   const bf16_t* Vh = V + hoff;
 
   const int qw0 = q0 + wave * 32;
-  const int myq = qw0 + l32;
+  const int myq = qw0 + (lane & 31);
   const bool wave_live = qw0 < N;
   const int wave_last_q = min(qw0 + 31, N - 1);
 
@@ -289,64 +343,78 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(
 
   const int last_row = min(q0 + T::B32, N) - 1;
   const int n_kblk = CAUSAL ? (last_row / T::BS + 1) : (N + T::BS - 1) / T::BS;
-  const int g16 = lane >> 4, j16 = lane & 15, dsub = g16 & 1;
+  const int n_wave = !wave_live ? 0 : (CAUSAL ? min(n_kblk, wave_last_q / T::BS + 1) : n_kblk);
 
-  TilePair<D> pair;
-  pair.load(Kh, Vh, 0, N, tid);
-  pair.store(smem, smem + T::TILE, tid);
-  for (int j = 0; j < n_kblk; ++j) {
-    if (j + 1 < n_kblk) pair.load(Kh, Vh, (j + 1) * T::BS, N, tid);
-    __syncthreads();
-    const bf16_t* Ks = smem + (j & 1) * T::STAGE;
-    const bf16_t* Vs = Ks + T::TILE;
-    const int kb0 = j * T::BS;
+  const TileReader<D> rd = make_reader<D>(lane);
+  int ldoff[T::PER];
+  tile_offsets<D, T::BS, T::NT>(ldoff, wave, lane);
+  auto ktile = [&](int slot) { return smem + slot * 2 * T::TILE; };
+  auto vtile = [&](int slot) { return smem + slot * 2 * T::TILE + T::TILE; };
 
-    if (wave_live && (!CAUSAL || kb0 <= wave_last_q)) {
-      f32x16 s[T::BS / 32], dp[T::BS / 32];
+  // S^T = K Q^T and dP^T = V dO^T for one 32-key subtile (lane = query)
+  auto sdp = [&](const bf16_t* Ks, const bf16_t* Vs, int sub, f32x16& sacc, f32x16& dacc) {
+    sacc = zero16();
+    dacc = zero16();
 #pragma unroll
-      for (int t = 0; t < T::BS / 32; ++t) {
-        s[t] = zero16();
-        dp[t] = zero16();
-      }
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-#pragma unroll
-        for (int t = 0; t < T::BS / 32; ++t) {
-          const bf16x8 ak = lds_load8(Ks + (t * 32 + l32) * T::RS + kk * 16 + hi * 8);
-          const bf16x8 av = lds_load8(Vs + (t * 32 + l32) * T::RS + kk * 16 + hi * 8);
-          s[t] = mfma32x32x16(ak, qf[kk], s[t]);
-          dp[t] = mfma32x32x16(av, dof[kk], dp[t]);
-        }
-      }
-      // Entry (t, i): key kb0 + 32 t + 8 (i/4) + 4 hi + i%4, query myq.
-      const bool edge = (kb0 + T::BS > N) || (CAUSAL && kb0 + T::BS - 1 > qw0);
-#pragma unroll
-      for (int t = 0; t < T::BS / 32; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = exp2_fast(__builtin_fmaf(s[t][i], c2, -lse2));
-          if (edge) {
-            const int key = kb0 + t * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
-            if (key >= N || (CAUSAL && key > myq)) p = 0.0f;
-          }
-          dp[t][i] = p * (dp[t][i] - dq_d);
-        }
-      bf16x8 sb[T::BS / 16];
-#pragma unroll
-      for (int ks = 0; ks < T::BS / 16; ++ks) sb[ks] = pack8(dp[ks >> 1], (ks & 1) * 8);
-#pragma unroll
-      for (int ks = 0; ks < T::BS / 16; ++ks) {
-        const int row_lo = ks * 16 + 4 * hi + (j16 >> 2);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const int col = dt * 32 + 16 * dsub + 4 * (j16 & 3);
-          const bf16x8 a_k = join8(lds_load_tr4(Ks + row_lo * T::RS + col),
-                                   lds_load_tr4(Ks + (row_lo + 8) * T::RS + col));
-          dq[dt] = mfma32x32x16(a_k, sb[ks], dq[dt]);
-        }
-      }
+    for (int kk = 0; kk < D / 16; ++kk) {
+      sacc = mfma32x32x16(rd.row8(Ks, sub, kk), qf[kk], sacc);
+      dacc = mfma32x32x16(rd.row8(Vs, sub, kk), dof[kk], dacc);
     }
-    if (j + 1 < n_kblk) pair.store(smem + ((j + 1) & 1) * T::STAGE, smem + ((j + 1) & 1) * T::STAGE + T::TILE, tid);
+  };
+  auto elementwise = [&](int kb0, int sub, const f32x16& sacc, const f32x16& dacc, bf16x8* sb, bool edge) {
+    f32x16 ds;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float pv = exp2_fast(__builtin_fmaf(sacc[i], c2, -lse2));
+      if (edge) {
+        const int key = kb0 + sub * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
+        if (key >= N || (CAUSAL && key > myq)) pv = 0.0f;
+      }
+      ds[i] = pv * (dacc[i] - dq_d);
+    }
+    sb[0] = pack8(ds, 0);
+    sb[1] = pack8(ds, 8);
+  };
+  // dQ^T += K^T dS^T for one subtile
+  auto grads = [&](const bf16_t* Ks, int sub, const bf16x8* sb) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) dq[dt] = mfma32x32x16(rd.col8(Ks, sub, ks, dt), sb[ks], dq[dt]);
+  };
+
+  load_tile<D, T::BS, T::NT>(ldoff, Kh, 0, N, ktile(0), wave, lane);
+  load_tile<D, T::BS, T::NT>(ldoff, Vh, 0, N, vtile(0), wave, lane);
+  wait_vmem();
+  zero_tail<D, T::BS, T::NT>(0, N, ktile(0), wave, lane);
+  zero_tail<D, T::BS, T::NT>(0, N, vtile(0), wave, lane);
+  __syncthreads();
+  for (int j = 0; j < n_kblk; ++j) {
+    const int slot = j & 1;
+    if (j + 1 < n_kblk) {
+      load_tile<D, T::BS, T::NT>(ldoff, Kh, (j + 1) * T::BS, N, ktile(slot ^ 1), wave, lane);
+      load_tile<D, T::BS, T::NT>(ldoff, Vh, (j + 1) * T::BS, N, vtile(slot ^ 1), wave, lane);
+    }
+    if (j < n_wave) {
+      const bf16_t* Ks = ktile(slot);
+      const bf16_t* Vs = vtile(slot);
+      const int kb0 = j * T::BS;
+      const bool edge = (kb0 + T::BS > N) || (CAUSAL && kb0 + T::BS - 1 > qw0);
+      f32x16 s0, d0, s1, d1;
+      bf16x8 sb0[2], sb1[2];
+      sdp(Ks, Vs, 0, s0, d0);
+      sdp(Ks, Vs, 1, s1, d1);
+      elementwise(kb0, 0, s0, d0, sb0, edge);
+      grads(Ks, 0, sb0);
+      elementwise(kb0, 1, s1, d1, sb1, edge);
+      grads(Ks, 1, sb1);
+    }
+    wait_vmem();
+    if (j + 1 < n_kblk) {
+      zero_tail<D, T::BS, T::NT>((j + 1) * T::BS, N, ktile(slot ^ 1), wave, lane);
+      zero_tail<D, T::BS, T::NT>((j + 1) * T::BS, N, vtile(slot ^ 1), wave, lane);
+    }
+    __syncthreads();
   }
 
   if (wave_live && myq < N) store_row_bf16<D>(dQ + hoff + (size_t)myq * D, dq, scale, hi);
@@ -366,7 +434,7 @@ hipError_t launch_dot_t(const BwdArgs& a, hipStream_t s) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
-  const int n_kblk = (a.N + BwdTile<D>::B32 - 1) / BwdTile<D>::B32;
+  const int n_kblk = (a.N + DkdvTile<D>::B32 - 1) / DkdvTile<D>::B32;
   const long long total = (long long)a.B * a.H * n_kblk;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)total), dim3(256), 0, s,
                      (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.dout,
@@ -377,7 +445,7 @@ hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
-  const int n_qblk = (a.N + BwdTile<D>::B32 - 1) / BwdTile<D>::B32;
+  const int n_qblk = (a.N + DqTile<D>::B32 - 1) / DqTile<D>::B32;
   const long long total = (long long)a.B * a.H * n_qblk;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)total), dim3(256), 0, s,
                      (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.dout,
