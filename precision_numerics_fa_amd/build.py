@@ -2,12 +2,15 @@
 
     python -m precision_numerics_fa_amd.build [--verbose]
 
-One hipcc invocation compiles the kernels and the C ABI into
-precision_numerics_fa_amd/libfa.so.  Packed FP32 VALU instructions are
-disabled for all device code (-packed-fp32-ops).  Floating-point contraction
-is off: a multiply-add is fused only where the source calls fmaf, so every
-rounding site is the one written in the kernel (and the stabilised and plain
-kernel instances round identically on rows the shift never touches).
+Each source is compiled to an object by hipcc (in parallel), and the objects
+are linked into precision_numerics_fa_amd/libfa.so.  Packed FP32 VALU
+instructions are disabled for all device code (-packed-fp32-ops).
+Floating-point contraction is off: a multiply-add is fused only where the
+source calls fmaf, so every rounding site is the one written in the kernel
+(and the stabilised and plain kernel instances round identically on rows the
+shift never touches).  The inline-assembly HBM->LDS copies name M0 as clobbered
+(-Wno-inline-asm silences the note that M0 is a reserved register: the
+compiler keeps no value of its own in M0 across them).
 """
 from __future__ import annotations
 
@@ -15,6 +18,7 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -32,23 +36,45 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
-def command(out: str = LIB, extra=()) -> list:
-    return [hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-shared", "-fPIC",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-ffp-contract=off",
-            "-Wall", "-Wno-unused-function",
-            "-I", INCLUDE, "-I", CSRC, *extra,
-            *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
+COMMON = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-ffp-contract=off", "-Wall", "-Wno-unused-function", "-Wno-inline-asm"]
+PER_SOURCE = {}
+NOISE = "is not a recognized feature for this target"
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln and ln.strip()]
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
+def compile_commands(objdir: str) -> list:
+    return [[hipcc(), *COMMON, "-I", INCLUDE, "-I", CSRC, *PER_SOURCE.get(src, []),
+             "-c", os.path.join(CSRC, src), "-o", os.path.join(objdir, src + ".o")] for src in SOURCES]
+
+
+def link_command(objdir: str, out: str) -> list:
+    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC",
+            *[os.path.join(objdir, s + ".o") for s in SOURCES], "-o", out]
+
+
+def _run(cmds: list) -> list:
+    procs = [subprocess.Popen(c, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True) for c in cmds]
+    msgs = []
+    for cmd, p in zip(cmds, procs):
+        out, _ = p.communicate()
+        lines = [ln for ln in out.splitlines() if NOISE not in ln and ln.strip()]
+        if p.returncode != 0:
+            raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(lines))
+        msgs += lines
+    return msgs
+
+
+def build(verbose: bool = False, out: str = LIB) -> str:
+    tmp = out + ".tmp"
+    objdir = tempfile.mkdtemp(prefix="fa_build_")
+    try:
+        cmds = compile_commands(objdir)
+        msgs = _run(cmds)
+        link = link_command(objdir, tmp)
+        msgs += _run([link])
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
     # a kernel whose host-side launch stub was not emitted would only fail
     # when the library is loaded; refuse such a build here
     nm = shutil.which("nm")
@@ -58,13 +84,15 @@ def build(verbose: bool = False) -> str:
         if missing:
             os.remove(tmp)
             raise RuntimeError("hipcc produced a library with undefined kernel stubs: " + ", ".join(missing[:4]))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(" ".join(cmd))
+        for c in cmds + [link]:
+            print(" ".join(c))
         for ln in msgs:
             print(ln)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
+    args = [a for a in sys.argv[1:] if not a.startswith("--")]
+    print(build(verbose="--verbose" in sys.argv, out=os.path.abspath(args[0]) if args else LIB))

@@ -175,6 +175,45 @@ __device__ __forceinline__ void load_tile(const int* off, const bf16_t* __restri
   }
 }
 
+// One direct global -> LDS copy of 16 bytes per lane: lane i's bytes land at
+// LDS byte address lds_base + 16 i and come from gbase + voff (gbase and
+// lds_base wave-uniform; lds_base travels in M0).  Written as inline assembly
+// so that the compiler does not treat the LDS writes as pending stores that
+// every later LDS read has to wait for: the caller waits (s_waitcnt vmcnt)
+// and synchronises the workgroup before anyone reads the tile.  The global
+// base stays in scalar registers, so a lane holds a single 32-bit offset.
+__device__ __forceinline__ void dma16(const bf16_t* gbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds_base)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// Rows [r0, r0 + ROWS) of X (N rows) into a swizzled tile with dma16 (r0 and
+// tile wave-uniform, r0 < N).  Rows past N read row N-1 (in bounds);
+// zero_tail() clears them afterwards.  off[] from tile_offsets().
+template <int D, int ROWS, int NT>
+__device__ __forceinline__ void load_tile_async(const int* off, const bf16_t* __restrict__ X, int r0, int N,
+                                                bf16_t* tile, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int PER_LANE = ROWS * CPR / NT;
+  const bf16_t* base = X + (size_t)r0 * D;
+  if (r0 + ROWS <= N) {
+#pragma unroll
+    for (int r = 0; r < PER_LANE; ++r)
+      dma16(base, (uint32_t)off[r] * 2u, lds_addr(tile + (r * NT + wave * 64) * 8));
+  } else {
+#pragma unroll
+    for (int r = 0; r < PER_LANE; ++r) {
+      const int c = r * NT + wave * 64 + lane;
+      const int row = c / CPR;
+      const int k = (c % CPR) ^ swz<D>(row);
+      const int src = min(r0 + row, N - 1) - r0;
+      dma16(base, (uint32_t)(src * D + k * 8) * 2u, lds_addr(tile + (r * NT + wave * 64) * 8));
+    }
+  }
+}
+
 // Zero the rows of a swizzled tile that lie past N (after its loads landed).
 template <int D, int ROWS, int NT>
 __device__ __forceinline__ void zero_tail(int r0, int N, bf16_t* tile, int wave, int lane) {

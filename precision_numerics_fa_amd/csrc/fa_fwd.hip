@@ -161,7 +161,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
       const bool btie = (b2 == bm) && (bm > kNegInf);
       // Running count >= 2: a new maximum restarts the count with this
       // block's; an equal maximum adds to it; a smaller one leaves it.
-      st.tied = (bm > st.m) ? btie : ((bm == st.m && bm > kNegInf) ? true : st.tied);
+      // (Bitwise, so that no branch splits the block.)
+      const bool gt = bm > st.m;
+      const bool eq = (bm == st.m) & (bm > kNegInf);
+      st.tied = (gt & btie) | (!gt & (eq | st.tied));
     }
     const float m_new = __builtin_fmaxf(st.m, bm);
     const float R = m_new * c2;
@@ -214,9 +217,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   };
 
   // ---- prologue: K0, V0 (and K1) into LDS; scores of block 0
-  load_tile<D, T::BK, 256>(ldoff, Kh, 0, N, Kbuf, wave, lane);
-  load_tile<D, T::BK, 256>(ldoff, Vh, 0, N, Vbuf, wave, lane);
-  if (n_kblk > 1) load_tile<D, T::BK, 256>(ldoff, Kh, T::BK, N, Kbuf + T::TILE, wave, lane);
+  load_tile_async<D, T::BK, 256>(ldoff, Kh, 0, N, Kbuf, wave, lane);
+  load_tile_async<D, T::BK, 256>(ldoff, Vh, 0, N, Vbuf, wave, lane);
+  if (n_kblk > 1) load_tile_async<D, T::BK, 256>(ldoff, Kh, T::BK, N, Kbuf + T::TILE, wave, lane);
   wait_vmem();
   zero_tail<D, T::BK, 256>(0, N, Kbuf, wave, lane);
   zero_tail<D, T::BK, 256>(0, N, Vbuf, wave, lane);
@@ -233,8 +236,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
     // block j-1 used; both were released by the barrier that ended j-1.
     bf16_t* const kdst = Kbuf + (j & 1) * T::TILE;
     bf16_t* const vdst = Vbuf + ((j + 1) & 1) * T::TILE;
-    if (j + 2 < n_kblk) load_tile<D, T::BK, 256>(ldoff, Kh, (j + 2) * T::BK, N, kdst, wave, lane);
-    if (j + 1 < n_kblk) load_tile<D, T::BK, 256>(ldoff, Vh, (j + 1) * T::BK, N, vdst, wave, lane);
+    if (j + 2 < n_kblk) load_tile_async<D, T::BK, 256>(ldoff, Kh, (j + 2) * T::BK, N, kdst, wave, lane);
+    if (j + 1 < n_kblk) load_tile_async<D, T::BK, 256>(ldoff, Vh, (j + 1) * T::BK, N, vdst, wave, lane);
 
     if (j < n_wave) {
       const int kb0 = j * T::BK;
