@@ -14,20 +14,22 @@
 // errors through these quantities; the recipe itself is the standard one.
 //
 // Two compute kernels, no atomics, deterministic:
-//   bwd_dkdv: a workgroup owns 128 keys (32 per wave, kept in registers as
-//     B operands) and walks 64-query blocks of Q and dO staged in LDS.  It
-//     works in the S layout (rows = queries, lane = key), so P and dS are
-//     already B operands of dV^T = dO^T P and dK^T = Q^T dS, whose A
-//     operands dO^T and Q^T come from the row-major LDS tiles through the
-//     transposing LDS read.
+//   bwd_dkdv: a workgroup owns 128 keys (32 per wave; K rows in an LDS tile,
+//     V rows in registers as B operands) and walks 32-query blocks of Q and
+//     dO.  It works in the S layout (rows = queries, lane = key), so P and dS
+//     are already B operands of dV^T = dO^T P and dK^T = Q^T dS, whose A
+//     operands dO^T and Q^T come from the LDS tiles through the transposing
+//     LDS read.
 //   bwd_dq: a workgroup owns 128 queries (Q and dO rows in registers) and
 //     walks 64-key blocks of K and V in LDS.  It works in the S^T layout
 //     (lane = query), so dS^T is the B operand of dQ^T = K^T dS^T, whose A
 //     operand K^T is a transposing read of the K tile.
 // Scores and dP are recomputed in both (7 products instead of 5), which buys
-// determinism and no LDS round trip of P or dS.  The dQ kernel reads K and V
-// from swizzled tiles copied straight into LDS and overlaps the second key
-// subtile's S/dP products with the first subtile's elementwise work.
+// determinism and no LDS round trip of P or dS.  All tiles are swizzled and
+// copied straight from HBM into LDS, one block ahead.  Both kernels keep
+// their register footprint within two waves per SIMD: the MFMAs of one wave
+// then overlap the exponential and elementwise work of the other, which the
+// hardware arbitrates better than a single wave's own instruction order.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -60,50 +62,6 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const bf16_t* __restrict__
 }
 
 // ---------------------------------------------------------------- shared tiling
-// dK/dV kernel tiling: row-major tiles staged through registers with a
-// padded row stride (its simple addressing keeps the kernel's register
-// footprint within one wave per SIMD without extra accumulator moves).
-template <int D>
-struct DkdvTile {
-  static constexpr int B32 = 128;       // keys per workgroup: 4 waves x 32
-  static constexpr int BS = 64;         // query rows per block
-  static constexpr int RS = D + 16;     // LDS row stride (elements), friendly to transposing reads
-  static constexpr int TILE = BS * RS;
-  static constexpr int STAGE = 2 * TILE;
-  static constexpr int CHUNKS = BS * D / 8 / 256;
-  static_assert(CHUNKS >= 1 && BS * D / 8 % 256 == 0, "tile/thread mismatch");
-};
-
-// Stage two row-major (BS x D) bf16 tiles, rows [r0, r0 + BS) of X and Y,
-// zero past N.
-template <int D>
-struct TilePair {
-  uint4 xr[DkdvTile<D>::CHUNKS], yr[DkdvTile<D>::CHUNKS];
-  __device__ __forceinline__ void load(const bf16_t* X, const bf16_t* Y, int r0, int N, int tid) {
-#pragma unroll
-    for (int r = 0; r < DkdvTile<D>::CHUNKS; ++r) {
-      const int c = tid + 256 * r;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      if (r0 + row < N) {
-        xr[r] = *reinterpret_cast<const uint4*>(X + (size_t)(r0 + row) * D + col);
-        yr[r] = *reinterpret_cast<const uint4*>(Y + (size_t)(r0 + row) * D + col);
-      } else {
-        xr[r] = make_uint4(0, 0, 0, 0);
-        yr[r] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(bf16_t* Xs, bf16_t* Ys, int tid) const {
-#pragma unroll
-    for (int r = 0; r < DkdvTile<D>::CHUNKS; ++r) {
-      const int c = tid + 256 * r;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(Xs + row * DkdvTile<D>::RS + col) = xr[r];
-      *reinterpret_cast<uint4*>(Ys + row * DkdvTile<D>::RS + col) = yr[r];
-    }
-  }
-};
-
 __device__ __forceinline__ void load_rows_as_b(bf16x8* f, const bf16_t* rowp, bool valid, int hi, int nsteps) {
   for (int kk = 0; kk < nsteps; ++kk) {
     if (valid) {
@@ -129,142 +87,6 @@ __device__ __forceinline__ void store_row_bf16(bf16_t* rowp, const f32x16* acc, 
       *reinterpret_cast<uint2*>(rowp + t * 32 + g * 8 + 4 * hi) = w;
     }
 }
-
-// ---------------------------------------------------------------- dK, dV
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
-    bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int N, int n_kblk, int total_blocks,
-    int xcd_remap, float c2, float scale) {
-  using T = DkdvTile<D>;
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * T::STAGE];
-  __shared__ float lse_s[2][T::BS];
-  __shared__ float dd_s[2][T::BS];
-
-  int bid = blockIdx.x;
-  if (xcd_remap) bid = (bid & 7) * (total_blocks >> 3) + (bid >> 3);
-  const int bh = bid / n_kblk;
-  const int kb = bid - bh * n_kblk;  // causal: the first key blocks carry the most work
-  const int k0 = kb * T::B32;
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const size_t hoff = (size_t)bh * (size_t)N * D;
-  const bf16_t* Qh = Q + hoff;
-  const bf16_t* dOh = dO + hoff;
-  const float* LSEh = LSE + (size_t)bh * N;
-  const float* Dh = Dvec + (size_t)bh * N;
-
-  const int kw0 = k0 + wave * 32;
-  const int myk = kw0 + l32;
-  const bool wave_live = kw0 < N;
-
-  // This wave's K and V rows as B operands (n = key, k = d).
-  bf16x8 kf[D / 16], vf[D / 16];
-  load_rows_as_b(kf, K + hoff + (size_t)myk * D, myk < N, hi, D / 16);
-  load_rows_as_b(vf, V + hoff + (size_t)myk * D, myk < N, hi, D / 16);
-
-  f32x16 dk[D / 32], dv[D / 32];
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t) {
-    dk[t] = zero16();
-    dv[t] = zero16();
-  }
-
-  const int q_first = CAUSAL ? k0 : 0;  // earlier queries see none of these keys
-  const int qb_first = q_first / T::BS;
-  const int qb_last = (N - 1) / T::BS;
-  const int g16 = lane >> 4, j16 = lane & 15, dsub = g16 & 1;
-
-  TilePair<D> pair;
-  float lse_r = 0.0f, dd_r = 0.0f;
-  auto gload = [&](int qb) {
-    pair.load(Qh, dOh, qb * T::BS, N, tid);
-    if (tid < T::BS) {
-      const int q = qb * T::BS + tid;
-      lse_r = q < N ? LSEh[q] * kLog2e : __builtin_huge_valf();  // P = 0 for rows past N
-      dd_r = q < N ? Dh[q] : 0.0f;
-    }
-  };
-  auto lstore = [&](int st) {
-    bf16_t* Qs = smem + st * T::STAGE;
-    pair.store(Qs, Qs + T::TILE, tid);
-    if (tid < T::BS) {
-      lse_s[st][tid] = lse_r;
-      dd_s[st][tid] = dd_r;
-    }
-  };
-
-  gload(qb_first);
-  lstore(0);
-  for (int qb = qb_first, it = 0; qb <= qb_last; ++qb, ++it) {
-    const int st = it & 1;
-    if (qb < qb_last) gload(qb + 1);
-    __syncthreads();
-    const bf16_t* Qs = smem + st * T::STAGE;
-    const bf16_t* dOs = Qs + T::TILE;
-
-    if (wave_live) {
-#pragma unroll
-      for (int qt = 0; qt < T::BS / 32; ++qt) {
-        const int qt0 = qb * T::BS + qt * 32;
-        if (CAUSAL && qt0 + 31 < kw0) continue;  // every query here precedes every key
-        f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const bf16x8 aq = lds_load8(Qs + (qt * 32 + l32) * T::RS + kk * 16 + hi * 8);
-          const bf16x8 ado = lds_load8(dOs + (qt * 32 + l32) * T::RS + kk * 16 + hi * 8);
-          s = mfma32x32x16(aq, kf[kk], s);
-          dp = mfma32x32x16(ado, vf[kk], dp);
-        }
-        // Entry i: query qt0 + 8 (i/4) + 4 hi + i%4, key myk.
-        const bool edge = CAUSAL && (qt0 < kw0 + 31);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ql = qt * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
-          float p = exp2_fast(__builtin_fmaf(s[i], c2, -lse_s[st][ql]));
-          if (edge && (qb * T::BS + ql < myk)) p = 0.0f;
-          s[i] = p;
-          dp[i] = p * (dp[i] - dd_s[st][ql]);
-        }
-        const bf16x8 pb0 = pack8(s, 0), pb1 = pack8(s, 8);
-        const bf16x8 sb0 = pack8(dp, 0), sb1 = pack8(dp, 8);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int row_lo = qt * 32 + ks * 16 + 4 * hi + (j16 >> 2);
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) {
-            const int col = dt * 32 + 16 * dsub + 4 * (j16 & 3);
-            const bf16x8 a_do = join8(lds_load_tr4(dOs + row_lo * T::RS + col),
-                                      lds_load_tr4(dOs + (row_lo + 8) * T::RS + col));
-            const bf16x8 a_q = join8(lds_load_tr4(Qs + row_lo * T::RS + col),
-                                     lds_load_tr4(Qs + (row_lo + 8) * T::RS + col));
-            dv[dt] = mfma32x32x16(a_do, ks ? pb1 : pb0, dv[dt]);
-            dk[dt] = mfma32x32x16(a_q, ks ? sb1 : sb0, dk[dt]);
-          }
-        }
-      }
-    }
-    if (qb < qb_last) lstore(st ^ 1);
-  }
-
-  if (wave_live && myk < N) {
-    store_row_bf16<D>(dK + hoff + (size_t)myk * D, dk, scale, hi);
-    store_row_bf16<D>(dV + hoff + (size_t)myk * D, dv, 1.0f, hi);
-  }
-}
-
-// dQ kernel tiling: swizzled tiles loaded straight into LDS.
-template <int D>
-struct DqTile {
-  static constexpr int B32 = 128;          // queries per workgroup: 4 waves x 32
-  static constexpr int BS = 64;            // keys per block (two 32-key subtiles)
-  static constexpr int TILE = BS * D;      // one swizzled tile (elements)
-  static constexpr int NT = 256;
-  static constexpr int PER = BS * D / 8 / NT;  // 16-byte loads per lane per tile
-};
 
 // Lane constants for reading a swizzled (64 x D) tile: the row-major operand
 // read (row sub*32 + l32, chunk 2 kk + hi) and the transposing read (row
@@ -302,9 +124,177 @@ __device__ __forceinline__ TileReader<D> make_reader(int lane) {
   return r;
 }
 
+// dK/dV kernel tiling: the workgroup's 128 K rows stay in one swizzled LDS
+// tile for the whole kernel; blocks of 32 query rows of Q and dO (and their
+// LSE and D) are copied straight into a ring of two LDS stages.
+template <int D>
+struct DkdvTile {
+  static constexpr int B32 = 128;              // keys per workgroup: 4 waves x 32
+  static constexpr int BS = 32;                // query rows per block
+  static constexpr int TILE = BS * D;          // one swizzled Q or dO tile (elements)
+  static constexpr int NT = 256;
+  static constexpr int PER = BS * D / 8 / NT;  // 16-byte copies per lane per tile
+  static constexpr int KPER = B32 * D / 8 / NT;
+};
+
+// ---------------------------------------------------------------- dK, dV
+// A workgroup owns 128 keys, 32 per wave.  Per 32-query block a wave forms
+// S = Q K^T (K rows from the LDS tile) and dP = dO V^T (V rows in
+// registers) in the S layout (rows = queries, lane = key), so P and dS are
+// already B operands of dV^T = dO^T P and dK^T = Q^T dS, whose A operands
+// dO^T and Q^T come from the swizzled tiles through the transposing LDS read.
+// The register footprint allows two waves per SIMD.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
+    bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int N, int n_kblk, int total_blocks,
+    int xcd_remap, float c2, float scale) {
+  using T = DkdvTile<D>;
+  __shared__ __attribute__((aligned(16))) bf16_t ktile[T::B32 * D];
+  // two stages of (Q tile, dO tile) and of (LSE, D) for the block's rows
+  __shared__ __attribute__((aligned(16))) bf16_t tiles[2][2 * T::TILE];
+  __shared__ __attribute__((aligned(16))) float vecs[2][2 * T::BS];
+
+  int bid = blockIdx.x;
+  if (xcd_remap) bid = (bid & 7) * (total_blocks >> 3) + (bid >> 3);
+  const int bh = bid / n_kblk;
+  const int kb = bid - bh * n_kblk;  // causal: the first key blocks carry the most work
+  const int k0 = kb * T::B32;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const size_t hoff = (size_t)bh * (size_t)N * D;
+  const bf16_t* Qh = Q + hoff;
+  const bf16_t* dOh = dO + hoff;
+  const float* LSEh = LSE + (size_t)bh * N;
+  const float* Dh = Dvec + (size_t)bh * N;
+
+  const int kw0 = k0 + wave * 32;
+  const int myk = kw0 + l32;
+  const bool wave_live = kw0 < N;
+
+  // This wave's V rows as B operands (n = key, k = d).
+  bf16x8 vf[D / 16];
+  load_rows_as_b(vf, V + hoff + (size_t)myk * D, myk < N, hi, D / 16);
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    dk[t] = zero16();
+    dv[t] = zero16();
+  }
+
+  const int q_first = CAUSAL ? k0 : 0;  // earlier queries see none of these keys
+  const int qb_first = q_first / T::BS;
+  const int qb_last = (N - 1) / T::BS;
+  const TileReader<D> rd = make_reader<D>(lane);
+  int ldoff[T::PER];
+  tile_offsets<D, T::BS, T::NT>(ldoff, wave, lane);
+
+  // Copies of block qb into stage stg: the Q and dO tiles, and LSE and D of
+  // its rows (wave 0; a block that crosses N takes plain loads and gives the
+  // rows past N LSE = +inf, so that their P and dS vanish).
+  auto issue = [&](int qb, int stg) {
+    const int r0 = qb * T::BS;
+    load_tile_async<D, T::BS, T::NT>(ldoff, Qh, r0, N, tiles[stg], wave, lane);
+    load_tile_async<D, T::BS, T::NT>(ldoff, dOh, r0, N, tiles[stg] + T::TILE, wave, lane);
+    if (wave == 0) {
+      if (r0 + T::BS <= N) {
+        if (lane < T::BS / 4)
+          dma16(reinterpret_cast<const bf16_t*>(LSEh + r0), lane * 16u, lds_addr(vecs[stg]));
+        else if (lane < T::BS / 2)
+          dma16(reinterpret_cast<const bf16_t*>(Dh + r0), (lane - T::BS / 4) * 16u, lds_addr(vecs[stg]));
+      } else if (lane < T::BS) {
+        const int q = r0 + lane;
+        vecs[stg][lane] = q < N ? LSEh[q] : __builtin_huge_valf();
+        vecs[stg][T::BS + lane] = q < N ? Dh[q] : 0.0f;
+      }
+    }
+  };
+  auto zero_tails = [&](int qb, int stg) {
+    zero_tail<D, T::BS, T::NT>(qb * T::BS, N, tiles[stg], wave, lane);
+    zero_tail<D, T::BS, T::NT>(qb * T::BS, N, tiles[stg] + T::TILE, wave, lane);
+  };
+
+  // One 32-query block: S, dP, then P and dS, then the dV and dK products.
+  // Entry i of S is query 8 (i/4) + 4 hi + i%4 of the block, key myk.
+  auto body = [&](bool edge, int qb, int stg) {
+    const bf16_t* Qs = tiles[stg];
+    const bf16_t* dOs = tiles[stg] + T::TILE;
+    const float* vec = vecs[stg];
+    f32x16 sacc = zero16(), dacc = zero16();
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      sacc = mfma32x32x16(rd.row8(Qs, 0, kk), rd.row8(ktile, wave, kk), sacc);
+      dacc = mfma32x32x16(rd.row8(dOs, 0, kk), vf[kk], dacc);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int ql = g * 8 + hi * 4;
+      const float4 l4 = *reinterpret_cast<const float4*>(vec + ql);
+      const float4 d4 = *reinterpret_cast<const float4*>(vec + T::BS + ql);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * g + e;
+        float p = exp2_fast(__builtin_fmaf(sacc[i], c2, -(lv[e] * kLog2e)));
+        if (edge && qb * T::BS + ql + e < myk) p = 0.0f;
+        sacc[i] = p;
+        dacc[i] = p * (dacc[i] - dv4[e]);
+      }
+    }
+    const bf16x8 pb[2] = {pack8(sacc, 0), pack8(sacc, 8)};
+    const bf16x8 sb[2] = {pack8(dacc, 0), pack8(dacc, 8)};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        dv[dt] = mfma32x32x16(rd.col8(dOs, 0, ks, dt), pb[ks], dv[dt]);
+        dk[dt] = mfma32x32x16(rd.col8(Qs, 0, ks, dt), sb[ks], dk[dt]);
+      }
+  };
+
+  // prologue: the K tile and the first block
+  int kofs[T::KPER];
+  tile_offsets<D, T::B32, T::NT>(kofs, wave, lane);
+  load_tile_async<D, T::B32, T::NT>(kofs, K + hoff, k0, N, ktile, wave, lane);
+  issue(qb_first, 0);
+  wait_vmem();
+  zero_tail<D, T::B32, T::NT>(k0, N, ktile, wave, lane);
+  zero_tails(qb_first, 0);
+  __syncthreads();
+  for (int qb = qb_first, it = 0; qb <= qb_last; ++qb, ++it) {
+    const int stg = it & 1;
+    if (qb < qb_last) issue(qb + 1, stg ^ 1);
+    // a wave skips blocks whose queries all precede its keys
+    if (wave_live && !(CAUSAL && qb * T::BS + T::BS - 1 < kw0))
+      body(CAUSAL && qb * T::BS < kw0 + 31, qb, stg);
+    wait_vmem();
+    if (qb < qb_last) zero_tails(qb + 1, stg ^ 1);
+    __syncthreads();
+  }
+
+  if (wave_live && myk < N) {
+    store_row_bf16<D>(dK + hoff + (size_t)myk * D, dk, scale, hi);
+    store_row_bf16<D>(dV + hoff + (size_t)myk * D, dv, 1.0f, hi);
+  }
+}
+
+// dQ kernel tiling: swizzled tiles loaded straight into LDS.
+template <int D>
+struct DqTile {
+  static constexpr int B32 = 128;          // queries per workgroup: 4 waves x 32
+  static constexpr int BS = 64;            // keys per block (two 32-key subtiles)
+  static constexpr int TILE = BS * D;      // one swizzled tile (elements)
+  static constexpr int NT = 256;
+  static constexpr int PER = BS * D / 8 / NT;  // 16-byte loads per lane per tile
+};
+
 // ---------------------------------------------------------------- dQ
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
     bf16_t* __restrict__ dQ, int N, int n_qblk, int total_blocks, int xcd_remap, float c2,
@@ -383,8 +373,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
       for (int dt = 0; dt < D / 32; ++dt) dq[dt] = mfma32x32x16(rd.col8(Ks, sub, ks, dt), sb[ks], dq[dt]);
   };
 
-  load_tile<D, T::BS, T::NT>(ldoff, Kh, 0, N, ktile(0), wave, lane);
-  load_tile<D, T::BS, T::NT>(ldoff, Vh, 0, N, vtile(0), wave, lane);
+  load_tile_async<D, T::BS, T::NT>(ldoff, Kh, 0, N, ktile(0), wave, lane);
+  load_tile_async<D, T::BS, T::NT>(ldoff, Vh, 0, N, vtile(0), wave, lane);
   wait_vmem();
   zero_tail<D, T::BS, T::NT>(0, N, ktile(0), wave, lane);
   zero_tail<D, T::BS, T::NT>(0, N, vtile(0), wave, lane);
@@ -392,22 +382,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   for (int j = 0; j < n_kblk; ++j) {
     const int slot = j & 1;
     if (j + 1 < n_kblk) {
-      load_tile<D, T::BS, T::NT>(ldoff, Kh, (j + 1) * T::BS, N, ktile(slot ^ 1), wave, lane);
-      load_tile<D, T::BS, T::NT>(ldoff, Vh, (j + 1) * T::BS, N, vtile(slot ^ 1), wave, lane);
+      load_tile_async<D, T::BS, T::NT>(ldoff, Kh, (j + 1) * T::BS, N, ktile(slot ^ 1), wave, lane);
+      load_tile_async<D, T::BS, T::NT>(ldoff, Vh, (j + 1) * T::BS, N, vtile(slot ^ 1), wave, lane);
     }
     if (j < n_wave) {
       const bf16_t* Ks = ktile(slot);
       const bf16_t* Vs = vtile(slot);
       const int kb0 = j * T::BS;
       const bool edge = (kb0 + T::BS > N) || (CAUSAL && kb0 + T::BS - 1 > qw0);
-      f32x16 s0, d0, s1, d1;
-      bf16x8 sb0[2], sb1[2];
-      sdp(Ks, Vs, 0, s0, d0);
-      sdp(Ks, Vs, 1, s1, d1);
-      elementwise(kb0, 0, s0, d0, sb0, edge);
-      grads(Ks, 0, sb0);
-      elementwise(kb0, 1, s1, d1, sb1, edge);
-      grads(Ks, 1, sb1);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        f32x16 s0, d0;
+        bf16x8 sb0[2];
+        sdp(Ks, Vs, sub, s0, d0);
+        elementwise(kb0, sub, s0, d0, sb0, edge);
+        grads(Ks, sub, sb0);
+      }
     }
     wait_vmem();
     if (j + 1 < n_kblk) {
