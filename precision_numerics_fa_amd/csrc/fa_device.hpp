@@ -175,6 +175,13 @@ __device__ __forceinline__ void load_tile(const int* off, const bf16_t* __restri
   }
 }
 
+// A copy of x the compiler cannot see through, so that values computed from
+// it in a rarely taken branch are not hoisted out of an enclosing loop.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // One direct global -> LDS copy of 16 bytes per lane: lane i's bytes land at
 // LDS byte address lds_base + 16 i and come from gbase + voff (gbase and
 // lds_base wave-uniform; lds_base travels in M0).  Written as inline assembly
@@ -203,9 +210,13 @@ __device__ __forceinline__ void load_tile_async(const int* off, const bf16_t* __
     for (int r = 0; r < PER_LANE; ++r)
       dma16(base, (uint32_t)off[r] * 2u, lds_addr(tile + (r * NT + wave * 64) * 8));
   } else {
+    // (the lane index passes through an opaque copy: the tail path's lane
+    // constants are then formed here, when the path runs, instead of being
+    // hoisted out of the caller's loop into registers held throughout)
+    const int ln = opaque(lane);
 #pragma unroll
     for (int r = 0; r < PER_LANE; ++r) {
-      const int c = r * NT + wave * 64 + lane;
+      const int c = r * NT + wave * 64 + ln;
       const int row = c / CPR;
       const int k = (c % CPR) ^ swz<D>(row);
       const int src = min(r0 + row, N - 1) - r0;
@@ -220,9 +231,10 @@ __device__ __forceinline__ void zero_tail(int r0, int N, bf16_t* tile, int wave,
   constexpr int CPR = D / 8;
   constexpr int PER_LANE = ROWS * CPR / NT;
   if (r0 + ROWS <= N) return;
+  const int ln = opaque(lane);
 #pragma unroll
   for (int r = 0; r < PER_LANE; ++r) {
-    const int c = r * NT + wave * 64 + lane;
+    const int c = r * NT + wave * 64 + ln;
     if (r0 + c / CPR >= N) *reinterpret_cast<uint4*>(tile + c * 8) = make_uint4(0, 0, 0, 0);
   }
 }
