@@ -206,9 +206,14 @@ __device__ __forceinline__ void load_tile_async(const int* off, const bf16_t* __
   constexpr int PER_LANE = ROWS * CPR / NT;
   const bf16_t* base = X + (size_t)r0 * D;
   if (r0 + ROWS <= N) {
+    // copy r covers rows r * (NT / CPR) + (the rows of copy 0), and the
+    // swizzle repeats every 16 rows: its offsets are copy 0's plus a
+    // uniform step, which goes into the scalar base
+    static_assert((NT / CPR) % 16 == 0, "swizzle period");
+    const uint32_t v0 = (uint32_t)off[0] * 2u;
 #pragma unroll
     for (int r = 0; r < PER_LANE; ++r)
-      dma16(base, (uint32_t)off[r] * 2u, lds_addr(tile + (r * NT + wave * 64) * 8));
+      dma16(base + r * (NT / CPR) * D, v0, lds_addr(tile + (r * NT + wave * 64) * 8));
   } else {
     // (the lane index passes through an opaque copy: the tail path's lane
     // constants are then formed here, when the path runs, instead of being
