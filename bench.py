@@ -7,6 +7,7 @@ HBM before the timed region.  The step is timed as a whole (synchronised wall
 clock) and each kernel with HIP events on the stream it is launched on.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+    python bench.py --sweep [--steps 20]      # per-workload forward/backward table
 
 Prints one JSON line.  FLOP are algorithmic: forward 4*B*H*N^2*d halved for
 causal; backward 2.5x the forward (five N^2 d products against two).
@@ -38,6 +39,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=48, help="heads the CPU oracle times")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step benchmark, time the forward (fix on and off) and the "
+                         "backward on every workload c1..c5 and print one JSON line per workload")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB a few times "
                          "(calibrates the HBM byte counters) and exit")
@@ -100,6 +104,9 @@ def main():
         copy_probe(args.copy_probe)
         return
     fa.load()
+    if args.sweep:
+        sweep(args)
+        return
 
     w = F.WORKLOADS["c4"].with_shape(with_do=True)
     B, H, N, d = w.B, w.H, w.N, w.d
@@ -218,6 +225,67 @@ def main():
     if not args.no_cpu_baseline:
         out.update(cpu_baseline_leg(w, full, o, lse, dq, dk, dv, args.cpu_heads, fwd_flop + bwd_flop))
     print(json.dumps(out), flush=True)
+
+
+def _timed(fn, reps):
+    import torch
+    for _ in range(max(2, reps // 5)):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def sweep(args):
+    """Forward (fix on, fix off) and backward throughput on every workload,
+    algorithmic FLOP and bytes as in the step benchmark."""
+    import numpy as np
+    import torch
+
+    import fa_inputs as F
+    import precision_numerics_fa_amd as fa
+
+    for name, w0 in F.WORKLOADS.items():
+        w = w0.with_shape(with_do=True)
+        B, H, N, d = w.B, w.H, w.N, w.d
+        full = F.full(w)
+        dev = {n: torch.from_numpy(full[n].view(np.int16)).view(torch.bfloat16).cuda()
+               for n in ("q", "k", "v", "do")}
+        del full
+        q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        reps = args.steps
+        fon = lambda: fa.fwd(q, k, v, causal=w.causal, stabilize=True, out=o, lse=lse)
+        foff = lambda: fa.fwd(q, k, v, causal=w.causal, stabilize=False, out=o, lse=lse)
+        _timed(fon, 4 * reps)  # clocks up
+        # fix on and off alternate; the fastest of three rounds each
+        t_on = min(_timed(fon, reps) for _ in range(3))
+        t_off = min(_timed(foff, reps) for _ in range(3))
+        t_on = min(t_on, *(_timed(fon, reps) for _ in range(2)))
+        fon()
+        t_bwd = min(_timed(lambda: fa.bwd(q, k, v, o, do, lse, causal=w.causal), reps) for _ in range(3))
+        pairs = N * (N + 1) / 2 if w.causal else N * N
+        fwd_flop = 4.0 * B * H * pairs * d
+        elem = B * H * N * d
+        fwd_bytes = 4 * elem * 2 + B * H * N * 4
+        rec = {"workload": name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+               "fwd_stab_ms": round(t_on, 4), "fwd_plain_ms": round(t_off, 4),
+               "fwd_tflops": round(fwd_flop / (t_on * 1e-3) / 1e12, 1),
+               "fwd_pct_peak": round(100 * fwd_flop / (t_on * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+               "fwd_gbs": round(fwd_bytes / (t_on * 1e-3) / 1e9, 1),
+               "stabilize_cost_pct": round(100 * (t_on / t_off - 1), 2),
+               "bwd_ms": round(t_bwd, 4),
+               "bwd_tflops": round(2.5 * fwd_flop / (t_bwd * 1e-3) / 1e12, 1),
+               "bwd_pct_peak": round(100 * 2.5 * fwd_flop / (t_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+        print(json.dumps(rec), flush=True)
+        del dev, q, k, v, do, o, lse
+        torch.cuda.empty_cache()
 
 
 def cpu_baseline_leg(w, full, o, lse, dq, dk, dv, heads, step_flop):
