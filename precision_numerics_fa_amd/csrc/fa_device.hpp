@@ -85,6 +85,15 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int base) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The values of x in lanes (l mod 32) and 32 + (l mod 32), in every lane l:
+// one v_permlane32_swap (gfx950) instead of an LDS permute.  Any symmetric
+// combination of the two (max, min, sum) is then the lane pair's.
+__device__ __forceinline__ void lane_pair(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Wait until at most N vector-memory loads of this wave are outstanding

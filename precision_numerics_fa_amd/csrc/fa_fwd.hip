@@ -153,11 +153,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
         if (STAB) m2 = __builtin_fmaxf(m2, __builtin_amdgcn_fmed3f(mx, x, y));
         mx = __builtin_fmaxf(mx, __builtin_fmaxf(x, y));
       }
-    const float omx = __shfl_xor(mx, 32);
-    const float bm = __builtin_fmaxf(mx, omx);
+    float mx_lo, mx_hi;
+    lane_pair(mx, mx_lo, mx_hi);
+    const float bm = __builtin_fmaxf(mx_lo, mx_hi);
     if (STAB) {
-      const float om2 = __shfl_xor(m2, 32);
-      const float b2 = __builtin_fmaxf(__builtin_fminf(mx, omx), __builtin_fmaxf(m2, om2));
+      float m2_lo, m2_hi;
+      lane_pair(m2, m2_lo, m2_hi);
+      const float b2 = __builtin_fmaxf(__builtin_fminf(mx_lo, mx_hi), __builtin_fmaxf(m2_lo, m2_hi));
       const bool btie = (b2 == bm) && (bm > kNegInf);
       // Running count >= 2: a new maximum restarts the count with this
       // block's; an equal maximum adds to it; a smaller one leaves it.
@@ -262,7 +264,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   }
 
   // ---- epilogue: O = O_bar / l (as O_bar * (1/l)), LSE = (M + log2 l) ln 2
-  const float lt = st.l + __shfl_xor(st.l, 32);
+  float l_lo, l_hi;
+  lane_pair(st.l, l_lo, l_hi);
+  const float lt = l_lo + l_hi;
   if (wave_live && myq < N) {
     const float rinv = 1.0f / lt;
     bf16_t* Orow = O + hoff + (size_t)myq * D;
