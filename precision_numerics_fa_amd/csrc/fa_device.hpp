@@ -96,11 +96,6 @@ __device__ __forceinline__ void lane_pair(float x, float& lo, float& hi) {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Wait until at most N vector-memory loads of this wave are outstanding
-// (loads retire in issue order, so the older ones have landed).
-template <int N>
-__device__ __forceinline__ void wait_vmem_n() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
-
 // ---------------------------------------------------------------------------
 // Swizzled LDS tiles.  A tile holds ROWS rows of D bf16 with no padding; the
 // 16-byte chunk k of row r is stored at chunk position k ^ swz<D>(r).  LDS has
@@ -130,30 +125,12 @@ __device__ __forceinline__ int tile_off(int row, int col) {
   return row * D + ((((col >> 3) ^ swz<D>(row))) << 3) + (col & 7);
 }
 
-// Issue direct global -> LDS loads of rows [r0, r0 + ROWS) of a (N, D) bf16
-// matrix into a swizzled tile (NT threads; wave and lane as in the caller).
-// Rows past N read row N-1 (in bounds); zero_tail() clears them afterwards.
-template <int D, int ROWS, int NT>
-__device__ __forceinline__ void dma_tile(const bf16_t* __restrict__ X, int r0, int N, bf16_t* tile,
-                                         int wave, int lane) {
-  constexpr int CPR = D / 8;                 // chunks per row
-  constexpr int PER_LANE = ROWS * CPR / NT;
-  static_assert(PER_LANE >= 1 && ROWS * CPR % NT == 0, "tile/thread mismatch");
-#pragma unroll
-  for (int r = 0; r < PER_LANE; ++r) {
-    const int base = r * NT + wave * 64;     // wave-uniform first chunk of this load
-    const int c = base + lane;               // physical chunk written by this lane
-    const int row = c / CPR;
-    const int k = (c % CPR) ^ swz<D>(row);   // logical chunk stored at that position
-    const int src_row = min(r0 + row, N - 1);
-    __builtin_amdgcn_global_load_lds(X + (size_t)src_row * D + k * 8,
-                                     (__attribute__((address_space(3))) void*)(tile + base * 8), 16, 0, 0);
-  }
-}
-
 // Per-lane element offsets (within a ROWS x D block of the source matrix) of
-// the chunks dma_tile copies.  For a block that lies fully inside N the copy
-// is then a wave-uniform base pointer plus a fixed per-lane offset.
+// the chunks a tile copy moves: copy r of lane `lane` in wave `wave` writes
+// physical chunk c = r*NT + wave*64 + lane of the tile, which holds logical
+// chunk (c % CPR) ^ swz(row) of row c / CPR.  For a block that lies fully
+// inside N the copy is then a wave-uniform base pointer plus a fixed
+// per-lane offset.
 template <int D, int ROWS, int NT>
 __device__ __forceinline__ void tile_offsets(int* off, int wave, int lane) {
   constexpr int CPR = D / 8;
@@ -163,24 +140,6 @@ __device__ __forceinline__ void tile_offsets(int* off, int wave, int lane) {
     const int c = r * NT + wave * 64 + lane;
     const int row = c / CPR;
     off[r] = row * D + (((c % CPR) ^ swz<D>(row)) << 3);
-  }
-}
-
-// Rows [r0, r0 + ROWS) of X (N rows) into a swizzled tile, using offsets
-// from tile_offsets(); a block crossing N takes the clamping path.
-template <int D, int ROWS, int NT>
-__device__ __forceinline__ void load_tile(const int* off, const bf16_t* __restrict__ X, int r0, int N,
-                                          bf16_t* tile, int wave, int lane) {
-  constexpr int PER_LANE = ROWS * (D / 8) / NT;
-  if (r0 + ROWS <= N) {
-    const bf16_t* base = X + (size_t)r0 * D;
-#pragma unroll
-    for (int r = 0; r < PER_LANE; ++r)
-      __builtin_amdgcn_global_load_lds(base + off[r],
-                                       (__attribute__((address_space(3))) void*)(tile + (r * NT + wave * 64) * 8),
-                                       16, 0, 0);
-  } else {
-    dma_tile<D, ROWS, NT>(X, r0, N, tile, wave, lane);
   }
 }
 
@@ -271,10 +230,5 @@ __device__ __forceinline__ float shift_delta(float R) {
 __device__ __forceinline__ float row_offset(float R, bool tied) {
   return R + shift_delta(R) * (tied ? 1.0f : 0.0f);
 }
-
-// Scheduling-group masks for __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedVALU = 0x002;
-constexpr int kSchedMFMA = 0x008;
-constexpr int kSchedDSRead = 0x100;
 
 }  // namespace fa

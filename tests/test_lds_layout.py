@@ -48,7 +48,7 @@ def test_swizzle_permutes_each_row(D):
 @pytest.mark.parametrize("D,rows,nt", [(64, 64, 256), (128, 64, 256), (128, 32, 256), (64, 32, 256),
                                        (128, 128, 256), (64, 128, 256)])
 def test_copy_pattern_writes_every_chunk_once(D, rows, nt):
-    """tile_offsets/dma_tile: lane `lane` of wave `wave`, copy r, writes the
+    """tile_offsets/load_tile_async: lane `lane` of wave `wave`, copy r, writes the
     physical chunk c = r*NT + wave*64 + lane and reads logical chunk
     (c % CPR) ^ swz(row) of row c / CPR."""
     cpr = D // 8
