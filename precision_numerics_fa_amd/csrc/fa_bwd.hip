@@ -88,39 +88,40 @@ __device__ __forceinline__ void store_row_bf16(bf16_t* rowp, const f32x16* acc, 
     }
 }
 
-// Lane constants for reading a swizzled (64 x D) tile: the row-major operand
-// read (row sub*32 + l32, chunk 2 kk + hi) and the transposing read (row
-// sub*32 + ks*16 + 8 r + 4 hi + j16/4, column dt*32 + 16 dsub + 4 (j16 % 4)).
-// The swizzle depends only on the row modulo 16.
+// Reads of a swizzled tile: the row-major operand read (row sub*32 + l32,
+// chunk 2 kk + hi) and the transposing read (rows sub*32 + ks*16 + 8 r +
+// 4 hi + j16/4, column dt*32 + 16 dsub + 4 (j16 % 4)).  Stepping the operand
+// read by kk flips byte-offset bits 5 and up (offset(kk) = offset(0) ^
+// (kk << 5)), and stepping a transposing read by dt flips bits 6 and up,
+// because the chunk index sits above the in-chunk bits and below the row
+// bits (the swizzle depends on the row modulo 16 only).  Three offset
+// registers replace one per step; fresh() launders them once per block so
+// that the XORs are formed there rather than hoisted into registers.
 template <int D>
-struct TileReader {
-  int rsw;                 // swizzle of the row-major operand row
-  int trow, tsw0, tsw1;    // transposing read: first row, swizzles of rows trow and trow + 8
-  int tcol;                // transposing read: column within a 32-wide d tile
-  int l32, hi;
-  __device__ __forceinline__ bf16x8 row8(const bf16_t* tile, int sub, int kk) const {
-    return lds_load8(tile + (sub * 32 + l32) * D + (((2 * kk + hi) ^ rsw) << 3));
+struct TileReaderX {
+  uint32_t r0, t0, t1;  // byte offsets: operand row l32 at kk = 0; rows trow, trow + 8 at dt = 0
+  __device__ __forceinline__ TileReaderX fresh() const {
+    return TileReaderX{(uint32_t)opaque((int)r0), (uint32_t)opaque((int)t0), (uint32_t)opaque((int)t1)};
   }
-  // 8 bf16 of column (dt*32 + lane's d) for the 16 rows sub*32 + ks*16 + (0..15)
+  __device__ __forceinline__ bf16x8 row8(const bf16_t* tile, int sub, int kk) const {
+    const char* base = reinterpret_cast<const char*>(tile + sub * 32 * D);
+    return lds_load8(reinterpret_cast<const bf16_t*>(base + (r0 ^ (uint32_t)(kk << 5))));
+  }
   __device__ __forceinline__ bf16x8 col8(const bf16_t* tile, int sub, int ks, int dt) const {
-    const bf16_t* base = tile + (sub * 32 + ks * 16) * D;
-    const int c = dt * 32 + tcol;
-    return join8(lds_load_tr4(base + trow * D + (((c >> 3) ^ tsw0) << 3) + (c & 7)),
-                 lds_load_tr4(base + (trow + 8) * D + (((c >> 3) ^ tsw1) << 3) + (c & 7)));
+    const char* base = reinterpret_cast<const char*>(tile + (sub * 32 + ks * 16) * D);
+    return join8(lds_load_tr4(reinterpret_cast<const bf16_t*>(base + (t0 ^ (uint32_t)(dt << 6)))),
+                 lds_load_tr4(reinterpret_cast<const bf16_t*>(base + (t1 ^ (uint32_t)(dt << 6)))));
   }
 };
 
 template <int D>
-__device__ __forceinline__ TileReader<D> make_reader(int lane) {
-  TileReader<D> r;
-  r.l32 = lane & 31;
-  r.hi = lane >> 5;
-  r.rsw = swz<D>(r.l32);
-  const int j16 = lane & 15, dsub = (lane >> 4) & 1;
-  r.trow = 4 * r.hi + (j16 >> 2);
-  r.tsw0 = swz<D>(r.trow);
-  r.tsw1 = swz<D>(r.trow + 8);
-  r.tcol = 16 * dsub + 4 * (j16 & 3);
+__device__ __forceinline__ TileReaderX<D> make_reader_x(int lane) {
+  const int l32 = lane & 31, hi = lane >> 5, j16 = lane & 15, dsub = (lane >> 4) & 1;
+  const int trow = 4 * hi + (j16 >> 2), tcol = 16 * dsub + 4 * (j16 & 3);
+  TileReaderX<D> r;
+  r.r0 = 2u * (uint32_t)tile_off<D>(l32, hi * 8);
+  r.t0 = 2u * (uint32_t)tile_off<D>(trow, tcol);
+  r.t1 = 2u * (uint32_t)tile_off<D>(trow + 8, tcol);
   return r;
 }
 
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   const int q_first = CAUSAL ? k0 : 0;  // earlier queries see none of these keys
   const int qb_first = q_first / T::BS;
   const int qb_last = (N - 1) / T::BS;
-  const TileReader<D> rd = make_reader<D>(lane);
+  const TileReaderX<D> rdx = make_reader_x<D>(lane);
   int ldoff[T::PER];
   tile_offsets<D, T::BS, T::NT>(ldoff, wave, lane);
 
@@ -208,10 +209,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
           dma16(reinterpret_cast<const bf16_t*>(Dh + r0), (lane - T::BS / 4) * 16u, lds_addr(vecs[stg]));
       } else if (lane < T::BS) {
         const int q = r0 + lane;
-        vecs[stg][lane] = q < N ? LSEh[q] : __builtin_huge_valf();
+        vecs[stg][lane] = q < N ? LSEh[q] * kLog2e : __builtin_huge_valf();
         vecs[stg][T::BS + lane] = q < N ? Dh[q] : 0.0f;
       }
     }
+  };
+  // Once wave 0's copies of block qb have landed: LSE -> LSE * log2(e) in
+  // place (the tail path stored it scaled already), so that the elementwise
+  // step takes the base-2 offset straight from LDS.
+  auto scale_lse = [&](int qb, int stg) {
+    if (wave == 0 && lane < T::BS && qb * T::BS + T::BS <= N) vecs[stg][lane] *= kLog2e;
   };
   auto zero_tails = [&](int qb, int stg) {
     zero_tail<D, T::BS, T::NT>(qb * T::BS, N, tiles[stg], wave, lane);
@@ -221,6 +228,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   // One 32-query block: S, dP, then P and dS, then the dV and dK products.
   // Entry i of S is query 8 (i/4) + 4 hi + i%4 of the block, key myk.
   auto body = [&](bool edge, int qb, int stg) {
+    const TileReaderX<D> rd = rdx.fresh();
     const bf16_t* Qs = tiles[stg];
     const bf16_t* dOs = tiles[stg] + T::TILE;
     const float* vec = vecs[stg];
@@ -230,20 +238,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
       sacc = mfma32x32x16(rd.row8(Qs, 0, kk), rd.row8(ktile, wave, kk), sacc);
       dacc = mfma32x32x16(rd.row8(dOs, 0, kk), vf[kk], dacc);
     }
+    // P = 2^(S c - LSE log2 e); the LDS copy of LSE is pre-scaled
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int ql = g * 8 + hi * 4;
-      const float4 l4 = *reinterpret_cast<const float4*>(vec + ql);
-      const float4 d4 = *reinterpret_cast<const float4*>(vec + T::BS + ql);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+      const float4 l4 = *reinterpret_cast<const float4*>(vec + g * 8 + hi * 4);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * g + e;
-        float p = exp2_fast(__builtin_fmaf(sacc[i], c2, -(lv[e] * kLog2e)));
-        if (edge && qb * T::BS + ql + e < myk) p = 0.0f;
-        sacc[i] = p;
-        dacc[i] = p * (dacc[i] - dv4[e]);
-      }
+      for (int e = 0; e < 4; ++e) sacc[4 * g + e] = exp2_fast(__builtin_fmaf(sacc[4 * g + e], c2, -lv[e]));
+    }
+    // on the diagonal, keys after the query get P = 0: entry i's query
+    // offset 8 (i/4) + i%4 below lim is masked (lim = 0 masks nothing)
+    const int lim = edge ? myk - qb * T::BS - hi * 4 : 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if ((i >> 2) * 8 + (i & 3) < lim) sacc[i] = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 d4 = *reinterpret_cast<const float4*>(vec + T::BS + g * 8 + hi * 4);
+      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dacc[4 * g + e] = sacc[4 * g + e] * (dacc[4 * g + e] - dv4[e]);
     }
     const bf16x8 pb[2] = {pack8(sacc, 0), pack8(sacc, 8)};
     const bf16x8 sb[2] = {pack8(dacc, 0), pack8(dacc, 8)};
@@ -264,15 +278,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   wait_vmem();
   zero_tail<D, T::B32, T::NT>(k0, N, ktile, wave, lane);
   zero_tails(qb_first, 0);
+  scale_lse(qb_first, 0);
   __syncthreads();
   for (int qb = qb_first, it = 0; qb <= qb_last; ++qb, ++it) {
     const int stg = it & 1;
     if (qb < qb_last) issue(qb + 1, stg ^ 1);
     // a wave skips blocks whose queries all precede its keys
-    if (wave_live && !(CAUSAL && qb * T::BS + T::BS - 1 < kw0))
-      body(CAUSAL && qb * T::BS < kw0 + 31, qb, stg);
+    // blocks on the diagonal mask keys after the query; the rest need no mask
+    if (wave_live && !(CAUSAL && qb * T::BS + T::BS - 1 < kw0)) body(CAUSAL && qb * T::BS < kw0 + 31, qb, stg);
     wait_vmem();
-    if (qb < qb_last) zero_tails(qb + 1, stg ^ 1);
+    if (qb < qb_last) {
+      zero_tails(qb + 1, stg ^ 1);
+      scale_lse(qb + 1, stg ^ 1);
+    }
     __syncthreads();
   }
 
@@ -335,14 +353,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const int n_kblk = CAUSAL ? (last_row / T::BS + 1) : (N + T::BS - 1) / T::BS;
   const int n_wave = !wave_live ? 0 : (CAUSAL ? min(n_kblk, wave_last_q / T::BS + 1) : n_kblk);
 
-  const TileReader<D> rd = make_reader<D>(lane);
+  const TileReaderX<D> rdx = make_reader_x<D>(lane);
   int ldoff[T::PER];
   tile_offsets<D, T::BS, T::NT>(ldoff, wave, lane);
   auto ktile = [&](int slot) { return smem + slot * 2 * T::TILE; };
   auto vtile = [&](int slot) { return smem + slot * 2 * T::TILE + T::TILE; };
 
   // S^T = K Q^T and dP^T = V dO^T for one 32-key subtile (lane = query)
-  auto sdp = [&](const bf16_t* Ks, const bf16_t* Vs, int sub, f32x16& sacc, f32x16& dacc) {
+  auto sdp = [&](const TileReaderX<D>& rd, const bf16_t* Ks, const bf16_t* Vs, int sub, f32x16& sacc, f32x16& dacc) {
     sacc = zero16();
     dacc = zero16();
 #pragma unroll
@@ -366,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     sb[1] = pack8(ds, 8);
   };
   // dQ^T += K^T dS^T for one subtile
-  auto grads = [&](const bf16_t* Ks, int sub, const bf16x8* sb) {
+  auto grads = [&](const TileReaderX<D>& rd, const bf16_t* Ks, int sub, const bf16x8* sb) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -390,13 +408,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       const bf16_t* Vs = vtile(slot);
       const int kb0 = j * T::BS;
       const bool edge = (kb0 + T::BS > N) || (CAUSAL && kb0 + T::BS - 1 > qw0);
+      const TileReaderX<D> rd = rdx.fresh();
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         f32x16 s0, d0;
         bf16x8 sb0[2];
-        sdp(Ks, Vs, sub, s0, d0);
+        sdp(rd, Ks, Vs, sub, s0, d0);
         elementwise(kb0, sub, s0, d0, sb0, edge);
-        grads(Ks, sub, sb0);
+        grads(rd, Ks, sub, sb0);
       }
     }
     wait_vmem();

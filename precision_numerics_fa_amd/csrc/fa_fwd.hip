@@ -105,20 +105,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
     }
   }
 
-  // LDS offsets that do not change from block to block.
-  // K operand (row t*32 + l32, chunk 2 kk + hi): swz depends on l32 only.
-  int koff[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = tile_off<D>(l32, kk * 16 + hi * 8);
-  // V^T operand by transposing reads: row ks*16 + 8 r + 4 hi + j16/4,
-  // column dt*32 + 16 dsub + 4 (j16 % 4); swz does not depend on ks.
+  // LDS byte offsets of the operand reads at step 0.  The K operand of step
+  // kk (row t*32 + l32, chunk 2 kk + hi) sits at offset ^ (kk << 5), and the
+  // V^T transposing read of d-tile dt (rows ks*16 + 8 r + 4 hi + j16/4,
+  // column dt*32 + 16 dsub + 4 (j16 % 4)) at offset ^ (dt << 6): the chunk
+  // index lies above the in-chunk bits and below the row bits, so the swizzle
+  // and the step combine by XOR.
   const int j16 = lane & 15, dsub = (lane >> 4) & 1;
-  int voff[2][D / 32];
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-      voff[r][dt] = tile_off<D>(8 * r + 4 * hi + (j16 >> 2), dt * 32 + 16 * dsub + 4 * (j16 & 3));
+  const uint32_t kx0 = 2u * (uint32_t)tile_off<D>(l32, hi * 8);
+  const uint32_t vx0 = 2u * (uint32_t)tile_off<D>(4 * hi + (j16 >> 2), 16 * dsub + 4 * (j16 & 3));
+  const uint32_t vx1 = 2u * (uint32_t)tile_off<D>(8 + 4 * hi + (j16 >> 2), 16 * dsub + 4 * (j16 & 3));
 
   int ldoff[T::BK * D / 8 / 256];
   tile_offsets<D, T::BK, 256>(ldoff, wave, lane);
@@ -128,15 +124,21 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) o[t] = zero16();
 
-  // S^T = K Q^T for one block, raw FP32 dot products.
+  // S^T = K Q^T for one block, raw FP32 dot products.  (The offsets pass an
+  // opaque copy per block, so that the XORs are formed here instead of being
+  // hoisted out of the block loop into one register per step.)
   auto scores = [&](const bf16_t* Ks, f32x16* s) {
+    const uint32_t kx = (uint32_t)opaque((int)kx0);
 #pragma unroll
     for (int t = 0; t < NS; ++t) s[t] = zero16();
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-      for (int t = 0; t < NS; ++t)
-        s[t] = mfma32x32x16(lds_load8(Ks + t * 32 * D + koff[kk]), qf[kk], s[t]);
+      for (int t = 0; t < NS; ++t) {
+        const char* base = reinterpret_cast<const char*>(Ks + t * 32 * D);
+        s[t] = mfma32x32x16(lds_load8(reinterpret_cast<const bf16_t*>(base + (kx ^ (uint32_t)(kk << 5)))), qf[kk],
+                            s[t]);
+      }
   };
 
   // Online softmax of one block held in s (masked already): updates the row
@@ -198,12 +200,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
 
   // O^T += V^T bf16(P)^T for one block.
   auto pv = [&](const bf16_t* Vs, const bf16x8* pb) {
+    const uint32_t va = (uint32_t)opaque((int)vx0), vb = (uint32_t)opaque((int)vx1);
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const bf16_t* base = Vs + ks * 16 * D;
-        const bf16x8 a = join8(lds_load_tr4(base + voff[0][dt]), lds_load_tr4(base + voff[1][dt]));
+        const char* base = reinterpret_cast<const char*>(Vs + ks * 16 * D);
+        const bf16x8 a = join8(lds_load_tr4(reinterpret_cast<const bf16_t*>(base + (va ^ (uint32_t)(dt << 6)))),
+                               lds_load_tr4(reinterpret_cast<const bf16_t*>(base + (vb ^ (uint32_t)(dt << 6)))));
         o[dt] = mfma32x32x16(a, pb[ks], o[dt]);
       }
   };
