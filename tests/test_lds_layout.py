@@ -109,3 +109,24 @@ def test_transposing_reads_are_conflict_free(D):
                 assert not (seen & b), (D, base, r, dt, half)
                 seen |= b
             assert len(seen) == BANKS
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_operand_read_steps_are_xor(D):
+    """The kernels address the operand read of step kk as offset(0) ^ (kk << 5)
+    bytes, with offset(0) that of row r, chunk hi (r any tile row, hi 0/1)."""
+    for row, hi in itertools.product(range(128), range(2)):
+        base = 2 * tile_off(D, row, hi * 8)
+        for kk in range(D // 16):
+            assert 2 * tile_off(D, row, kk * 16 + hi * 8) == base ^ (kk << 5), (D, row, hi, kk)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_transposing_read_steps_are_xor(D):
+    """The kernels address the transposing read of column tile dt as
+    offset(0) ^ (dt << 6) bytes, offset(0) that of column 16 dsub + 4 c."""
+    for row, dsub, c in itertools.product(range(128), range(2), range(4)):
+        col0 = 16 * dsub + 4 * c
+        base = 2 * tile_off(D, row, col0)
+        for dt in range(D // 32):
+            assert 2 * tile_off(D, row, dt * 32 + col0) == base ^ (dt << 6), (D, row, dsub, c, dt)
