@@ -276,6 +276,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   load_tile_async<D, T::B32, T::NT>(kofs, K + hoff, k0, N, ktile, wave, lane);
   issue(qb_first, 0);
   wait_vmem();
+  wait_vmem_tracked();
   zero_tail<D, T::B32, T::NT>(k0, N, ktile, wave, lane);
   zero_tails(qb_first, 0);
   scale_lse(qb_first, 0);
@@ -394,6 +395,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   load_tile_async<D, T::BS, T::NT>(ldoff, Kh, 0, N, ktile(0), wave, lane);
   load_tile_async<D, T::BS, T::NT>(ldoff, Vh, 0, N, vtile(0), wave, lane);
   wait_vmem();
+  wait_vmem_tracked();
   zero_tail<D, T::BS, T::NT>(0, N, ktile(0), wave, lane);
   zero_tail<D, T::BS, T::NT>(0, N, vtile(0), wave, lane);
   __syncthreads();

@@ -96,6 +96,15 @@ __device__ __forceinline__ void lane_pair(float x, float& lo, float& hi) {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// The same wait issued through the builtin, which the compiler's wait-count
+// tracking sees (the inline-asm form above is opaque to it).  Issued once
+// after the prologue's register loads have landed, it clears the compiler's
+// record of them; otherwise a path on which they might still be in flight
+// makes it place a vmcnt(0) wait inside the main loop, where it would also
+// wait for the tile prefetches issued there.  (gfx9 encoding: vmcnt 0,
+// expcnt 7, lgkmcnt 15.)
+__device__ __forceinline__ void wait_vmem_tracked() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // ---------------------------------------------------------------------------
 // Swizzled LDS tiles.  A tile holds ROWS rows of D bf16 with no padding; the
 // 16-byte chunk k of row r is stored at chunk position k ^ swz<D>(r).  LDS has

@@ -227,6 +227,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   load_tile_async<D, T::BK, 256>(ldoff, Vh, 0, N, Vbuf, wave, lane);
   if (n_kblk > 1) load_tile_async<D, T::BK, 256>(ldoff, Kh, T::BK, N, Kbuf + T::TILE, wave, lane);
   wait_vmem();
+  wait_vmem_tracked();
   zero_tail<D, T::BK, 256>(0, N, Kbuf, wave, lane);
   zero_tail<D, T::BK, 256>(0, N, Vbuf, wave, lane);
   if (n_kblk > 1) zero_tail<D, T::BK, 256>(T::BK, N, Kbuf + T::TILE, wave, lane);
