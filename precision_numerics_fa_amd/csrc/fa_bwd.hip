@@ -227,7 +227,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
 
   // One 32-query block: S, dP, then P and dS, then the dV and dK products.
   // Entry i of S is query 8 (i/4) + 4 hi + i%4 of the block, key myk.
-  auto body = [&](bool edge, int qb, int stg) {
+  // MASKED: the block may hold queries before some key of the wave.
+  auto body = [&](auto masked, bool edge, int qb, int stg) {
+    constexpr bool MASKED = decltype(masked)::value;
     const TileReaderX<D> rd = rdx.fresh();
     const bf16_t* Qs = tiles[stg];
     const bf16_t* dOs = tiles[stg] + T::TILE;
@@ -248,10 +250,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     }
     // on the diagonal, keys after the query get P = 0: entry i's query
     // offset 8 (i/4) + i%4 below lim is masked (lim = 0 masks nothing)
-    const int lim = edge ? myk - qb * T::BS - hi * 4 : 0;
+    if (MASKED) {
+      const int lim = edge ? myk - qb * T::BS - hi * 4 : 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if ((i >> 2) * 8 + (i & 3) < lim) sacc[i] = 0.0f;
+      for (int i = 0; i < 16; ++i)
+        if ((i >> 2) * 8 + (i & 3) < lim) sacc[i] = 0.0f;
+    }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const float4 d4 = *reinterpret_cast<const float4*>(vec + T::BS + g * 8 + hi * 4);
@@ -281,19 +285,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   zero_tails(qb_first, 0);
   scale_lse(qb_first, 0);
   __syncthreads();
-  for (int qb = qb_first, it = 0; qb <= qb_last; ++qb, ++it) {
-    const int stg = it & 1;
+  auto step = [&](int qb, auto masked) {
+    const int stg = (qb - qb_first) & 1;
     if (qb < qb_last) issue(qb + 1, stg ^ 1);
     // a wave skips blocks whose queries all precede its keys
     // blocks on the diagonal mask keys after the query; the rest need no mask
-    if (wave_live && !(CAUSAL && qb * T::BS + T::BS - 1 < kw0)) body(CAUSAL && qb * T::BS < kw0 + 31, qb, stg);
+    if (wave_live && !(CAUSAL && qb * T::BS + T::BS - 1 < kw0))
+      body(masked, CAUSAL && qb * T::BS < kw0 + 31, qb, stg);
     wait_vmem();
     if (qb < qb_last) {
       zero_tails(qb + 1, stg ^ 1);
       scale_lse(qb + 1, stg ^ 1);
     }
     __syncthreads();
-  }
+  };
+  // Causal: the blocks that start before the workgroup's last key sit on
+  // the diagonal and run with the mask; the rest run without it.
+  const int qb_plain = CAUSAL ? min(qb_last + 1, (k0 + T::B32 - 1 + T::BS - 1) / T::BS) : qb_first;
+  int qb = qb_first;
+  for (; qb < qb_plain; ++qb) step(qb, std::true_type{});
+  for (; qb <= qb_last; ++qb) step(qb, std::false_type{});
 
   if (wave_live && myk < N) {
     store_row_bf16<D>(dK + hoff + (size_t)myk * D, dk, scale, hi);
@@ -370,15 +381,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       dacc = mfma32x32x16(rd.row8(Vs, sub, kk), dof[kk], dacc);
     }
   };
-  auto elementwise = [&](int kb0, int sub, const f32x16& sacc, const f32x16& dacc, bf16x8* sb, bool edge) {
+  // MASKED: the block may hold keys past N or (causal) after some query.
+  auto elementwise = [&](auto masked, int kb0, int sub, const f32x16& sacc, const f32x16& dacc, bf16x8* sb,
+                         bool edge) {
+    // entry i is key kb0 + 32 sub + 4 hi + off(i), off(i) = 8 (i/4) + i%4;
+    // on an edge block the keys past N (and, causal, after the query) get
+    // P = 0: those with off(i) > lim.  A select per entry, no branch.
+    constexpr bool MASKED = decltype(masked)::value;
+    const int last_key = CAUSAL ? min(N - 1, myq) : N - 1;
+    const int lim = MASKED && edge ? last_key - (kb0 + sub * 32 + hi * 4) : 64;
     f32x16 ds;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float pv = exp2_fast(__builtin_fmaf(sacc[i], c2, -lse2));
-      if (edge) {
-        const int key = kb0 + sub * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
-        if (key >= N || (CAUSAL && key > myq)) pv = 0.0f;
-      }
+      if (MASKED && (i >> 2) * 8 + (i & 3) > lim) pv = 0.0f;
       ds[i] = pv * (dacc[i] - dq_d);
     }
     sb[0] = pack8(ds, 0);
@@ -399,7 +415,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   zero_tail<D, T::BS, T::NT>(0, N, ktile(0), wave, lane);
   zero_tail<D, T::BS, T::NT>(0, N, vtile(0), wave, lane);
   __syncthreads();
-  for (int j = 0; j < n_kblk; ++j) {
+  // One key block: prefetch the next, compute, then wait for the prefetch.
+  auto step = [&](int j, auto masked) {
     const int slot = j & 1;
     if (j + 1 < n_kblk) {
       load_tile_async<D, T::BS, T::NT>(ldoff, Kh, (j + 1) * T::BS, N, ktile(slot ^ 1), wave, lane);
@@ -416,7 +433,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         f32x16 s0, d0;
         bf16x8 sb0[2];
         sdp(rd, Ks, Vs, sub, s0, d0);
-        elementwise(kb0, sub, s0, d0, sb0, edge);
+        elementwise(masked, kb0, sub, s0, d0, sb0, edge);
         grads(rd, Ks, sub, sb0);
       }
     }
@@ -426,7 +443,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       zero_tail<D, T::BS, T::NT>((j + 1) * T::BS, N, vtile(slot ^ 1), wave, lane);
     }
     __syncthreads();
-  }
+  };
+  // The leading blocks hold only keys below N and below the workgroup's
+  // first query, so they run without the mask; the rest run with it.
+  const int n_plain = min(n_kblk, (CAUSAL ? min(N, q0 + 1) : N) / T::BS);
+  int j = 0;
+  for (; j < n_plain; ++j) step(j, std::false_type{});
+  for (; j < n_kblk; ++j) step(j, std::true_type{});
 
   if (wave_live && myq < N) store_row_bf16<D>(dQ + hoff + (size_t)myq * D, dq, scale, hi);
 }
