@@ -15,6 +15,7 @@ compiler keeps no value of its own in M0 across them).
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -38,7 +39,8 @@ def hipcc() -> str:
 
 COMMON = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-ffp-contract=off", "-Wall", "-Wno-unused-function", "-Wno-inline-asm"]
+          "-ffp-contract=off", "-Wall", "-Wno-unused-function", "-Wno-inline-asm",
+          "-Rpass-analysis=kernel-resource-usage"]
 PER_SOURCE = {}
 NOISE = "is not a recognized feature for this target"
 
@@ -65,12 +67,44 @@ def _run(cmds: list) -> list:
     return msgs
 
 
+RESOURCE = re.compile(r"remark: +(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|"
+                      r"Occupancy \[waves/SIMD\]): (\S+)")
+
+
+def kernel_resources(msgs: list) -> dict:
+    """Per-kernel registers, scratch and occupancy from the compiler's
+    kernel-resource-usage remarks."""
+    table, cur = {}, None
+    for ln in msgs:
+        m = RESOURCE.search(ln)
+        if not m:
+            continue
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            cur = table.setdefault(val, {})
+        elif cur is not None:
+            cur[key.split()[0]] = int(val)
+    return table
+
+
+def check_resources(table: dict) -> None:
+    """Refuse kernels that spill.  The tile copies are inline-asm loads the
+    compiler does not count; a spill reload inside a loop gets a partial
+    vmcnt wait computed without them, which is not a wait for the reload."""
+    spills = [k for k, v in table.items() if v.get("ScratchSize", 0) > 0]
+    if spills:
+        raise RuntimeError("kernels use scratch (register spills): " + ", ".join(spills))
+
+
 def build(verbose: bool = False, out: str = LIB) -> str:
     tmp = out + ".tmp"
     objdir = tempfile.mkdtemp(prefix="fa_build_")
     try:
         cmds = compile_commands(objdir)
         msgs = _run(cmds)
+        resources = kernel_resources(msgs)
+        msgs = [ln for ln in msgs if "kernel-resource-usage" not in ln]
+        check_resources(resources)
         link = link_command(objdir, tmp)
         msgs += _run([link])
     finally:
@@ -90,6 +124,8 @@ def build(verbose: bool = False, out: str = LIB) -> str:
             print(" ".join(c))
         for ln in msgs:
             print(ln)
+        for name, v in sorted(resources.items()):
+            print(f"{name}: {v}")
     return out
 
 

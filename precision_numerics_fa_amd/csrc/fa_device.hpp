@@ -215,11 +215,14 @@ __device__ __forceinline__ void zero_tail(int r0, int N, bf16_t* tile, int wave,
   constexpr int CPR = D / 8;
   constexpr int PER_LANE = ROWS * CPR / NT;
   if (r0 + ROWS <= N) return;
+  // (lane and the zero pass through opaque copies, so that neither the
+  // offsets nor a register quad of zeros is hoisted out of the caller's loop)
   const int ln = opaque(lane);
+  const uint32_t z = (uint32_t)opaque(0);
 #pragma unroll
   for (int r = 0; r < PER_LANE; ++r) {
     const int c = r * NT + wave * 64 + ln;
-    if (r0 + c / CPR >= N) *reinterpret_cast<uint4*>(tile + c * 8) = make_uint4(0, 0, 0, 0);
+    if (r0 + c / CPR >= N) *reinterpret_cast<uint4*>(tile + c * 8) = make_uint4(z, z, z, z);
   }
 }
 
