@@ -2,11 +2,13 @@
 
 This module is shared by the CPU oracle, the GPU parity tests and the
 benchmark.  It holds no attention arithmetic: it draws Gaussian tensors,
-rounds them to bfloat16 (round-to-nearest-even) and, for the tie-heavy
+rounds them to bfloat16 or IEEE binary16 (round-to-nearest-even, the
+workload's element type) and, for the tie-heavy
 workloads, copies one key row onto another so that a query row sees its
 largest score twice.  Picking which key to copy needs the raw dot products
-q.k of one head; they are taken in float64 on bf16-exact values (exact, so
-the order of summation cannot matter) and are used for nothing else.
+q.k of one head; they are taken in float64 on bf16- or binary16-exact values
+(exact, so the order of summation cannot matter) and are used for nothing
+else.
 
 Workloads (shapes from the attention layers the pages discuss: GPT-2 small
 and medium, Llama-2-7B, and page 1's "critical" N*B = 131072 shape):
@@ -16,6 +18,10 @@ and medium, Llama-2-7B, and page 1's "critical" N*B = 131072 shape):
   c3  B=64 H=16 N=2048 d=64  causal, K plus a shared rank-4 term (weight 0.5)
   c4  B=4  H=32 N=4096 d=128 causal, plain N(0,1)
   c5  B=16 H=16 N=1024 d=64  causal, 5% repeated-max rows, with dO
+
+and the same c2, c4 and c5 shapes in binary16 (c2h, c4h, c5h: own seeds),
+for the FP16 path (page 1 describes the bias and the fix for FP16 and BF16
+alike).
 
 Every (b, h) head is drawn from its own counter-seeded PCG64 stream
 ``default_rng([seed, b, h])`` so that any subset of heads can be rebuilt on
@@ -45,6 +51,7 @@ class Workload:
     lowrank_rank: int = 0         # rank of the shared component added to K
     lowrank_weight: float = 0.0
     with_do: bool = False         # also draw dO (backward workloads)
+    dtype: str = "bf16"           # element type of the tensors: "bf16" or "f16"
 
     @property
     def scale(self) -> float:
@@ -64,6 +71,9 @@ WORKLOADS: Dict[str, Workload] = {
     "c3": Workload("c3", 64, 16, 2048, 64, True, 1003, lowrank_rank=4, lowrank_weight=0.5),
     "c4": Workload("c4", 4, 32, 4096, 128, True, 1004),
     "c5": Workload("c5", 16, 16, 1024, 64, True, 1005, tie_frac=0.05, with_do=True),
+    "c2h": Workload("c2h", 8, 12, 1024, 64, True, 1012, qk_mult=4.0, tie_frac=0.05, dtype="f16"),
+    "c4h": Workload("c4h", 4, 32, 4096, 128, True, 1014, dtype="f16"),
+    "c5h": Workload("c5h", 16, 16, 1024, 64, True, 1015, tie_frac=0.05, with_do=True, dtype="f16"),
 }
 
 
@@ -86,6 +96,35 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> IEEE binary16 bit patterns (uint16), round to nearest even
+    (numpy's float16 conversion)."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of binary16 bit patterns to float32."""
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def encode(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 values -> 16-bit patterns of the element type."""
+    if dtype == "bf16":
+        return to_bf16_bits(x)
+    if dtype == "f16":
+        return to_f16_bits(x)
+    raise ValueError(f"unknown element type {dtype!r}")
+
+
+def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """16-bit patterns of the element type -> float32 (exact)."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(bits)
+    if dtype == "f16":
+        return f16_bits_to_f32(bits)
+    raise ValueError(f"unknown element type {dtype!r}")
+
+
 # ----------------------------------------------------------------------------
 # repeated-maximum construction
 # ----------------------------------------------------------------------------
@@ -96,11 +135,11 @@ def _visible(N: int, causal: bool, i: int) -> int:
 
 
 def _make_ties(q: np.ndarray, k_bits: np.ndarray, causal: bool, target: int,
-               rng: np.random.Generator) -> Tuple[np.ndarray, np.ndarray]:
+               rng: np.random.Generator, dtype: str = "bf16") -> Tuple[np.ndarray, np.ndarray]:
     """Copy key rows so that at least `target` query rows have a repeated max.
 
-    q: (N, d) float64 (bf16-exact values); k_bits: (N, d) uint16, edited in place
-    on a copy.  Returns (new k_bits, sorted array of every row whose maximum
+    q: (N, d) float64 (values exact in the element type); k_bits: (N, d)
+    uint16 patterns of that type, edited in place on a copy.  Returns (new k_bits, sorted array of every row whose maximum
     is attained at least twice at the end).  Copying K[a] ties every row whose
     argmax is a and that can see b, so the count includes such collateral rows
     and can exceed `target`.
@@ -116,8 +155,8 @@ def _make_ties(q: np.ndarray, k_bits: np.ndarray, causal: bool, target: int,
     """
     N, d = q.shape
     k_bits = k_bits.copy()
-    kf = bf16_bits_to_f32(k_bits).astype(np.float64)
-    s = q @ kf.T                                   # exact: bf16 products summed in fp64
+    kf = decode(k_bits, dtype).astype(np.float64)
+    s = q @ kf.T                                   # exact: 16-bit products summed in fp64
     if causal:
         s[np.triu_indices(N, 1)] = -np.inf
     rowmax = s.max(axis=1)
@@ -179,7 +218,8 @@ def _lowrank_factors(w: Workload) -> Tuple[np.ndarray, np.ndarray]:
 
 
 def head(w: Workload, b: int, h: int, lowrank: Optional[Tuple[np.ndarray, np.ndarray]] = None) -> Dict[str, np.ndarray]:
-    """Inputs of one (b, h) head as bf16 bit patterns, shape (N, d) each.
+    """Inputs of one (b, h) head as 16-bit patterns of the workload's element
+    type, shape (N, d) each.
 
     Keys: 'q', 'k', 'v' (and 'do' when the workload has a backward), plus
     'tie_rows' (rows whose maximum raw score repeats after the construction).
@@ -196,15 +236,15 @@ def head(w: Workload, b: int, h: int, lowrank: Optional[Tuple[np.ndarray, np.nda
     if w.lowrank_rank:
         fa, fb = lowrank if lowrank is not None else _lowrank_factors(w)
         k = (k.astype(np.float64) + w.lowrank_weight * (fa @ fb.T) / math.sqrt(w.lowrank_rank)).astype(np.float32)
-    out = {"q": to_bf16_bits(q), "k": to_bf16_bits(k), "v": to_bf16_bits(v)}
+    out = {"q": encode(q, w.dtype), "k": encode(k, w.dtype), "v": encode(v, w.dtype)}
     if do is not None:
-        out["do"] = to_bf16_bits(do)
+        out["do"] = encode(do, w.dtype)
     tie_rows = np.zeros(0, dtype=np.int64)
     if w.tie_frac > 0:
         target = int(round(w.tie_frac * w.N))
-        qf = bf16_bits_to_f32(out["q"]).astype(np.float64)
+        qf = decode(out["q"], w.dtype).astype(np.float64)
         trng = np.random.default_rng([w.seed, b, h, 0x71E])
-        out["k"], tie_rows = _make_ties(qf, out["k"], w.causal, target, trng)
+        out["k"], tie_rows = _make_ties(qf, out["k"], w.causal, target, trng, w.dtype)
     out["tie_rows"] = tie_rows
     return out
 
@@ -215,7 +255,8 @@ def heads(w: Workload, pairs: Iterable[Tuple[int, int]]) -> List[Dict[str, np.nd
 
 
 def full(w: Workload) -> Dict[str, np.ndarray]:
-    """Whole (B, H, N, d) bf16 tensors (uint16 bit patterns) plus tie rows per head."""
+    """Whole (B, H, N, d) tensors (uint16 patterns of the element type) plus
+    tie rows per head."""
     names = ["q", "k", "v"] + (["do"] if w.with_do else [])
     out = {n: np.empty((w.B, w.H, w.N, w.d), dtype=np.uint16) for n in names}
     ties = {}
@@ -240,7 +281,8 @@ def sample_pairs(w: Workload, count: int, seed: int = 0) -> List[Tuple[int, int]
     return [allp[i] for i in idx]
 
 
-def random_bf16(shape: Sequence[int], seed: int, mult: float = 1.0) -> np.ndarray:
-    """Plain N(0, mult^2) bf16 bit patterns for ad-hoc shapes (edge-case tests)."""
+def random_bf16(shape: Sequence[int], seed: int, mult: float = 1.0, dtype: str = "bf16") -> np.ndarray:
+    """Plain N(0, mult^2) 16-bit patterns (bf16 unless ``dtype`` says "f16")
+    for ad-hoc shapes (edge-case tests)."""
     rng = np.random.default_rng([seed, 0xEDCE])
-    return to_bf16_bits(rng.standard_normal(tuple(shape), dtype=np.float32) * np.float32(mult))
+    return encode(rng.standard_normal(tuple(shape), dtype=np.float32) * np.float32(mult), dtype)

@@ -28,8 +28,9 @@
  * `stabilize` is accepted by fa_bwd for symmetry and ignored.
  *
  * Conventions shared by every entry point
- *   - Q, K, V, O, dO, dQ, dK, dV: bf16, shape (B, H, N, d), contiguous
- *     row-major (d fastest), device pointers, 16-byte aligned.
+ *   - Q, K, V, O, dO, dQ, dK, dV: bf16 (or IEEE binary16 through the _ex
+ *     entry points), shape (B, H, N, d), contiguous row-major (d fastest),
+ *     device pointers, 16-byte aligned.
  *   - LSE (and the workspace's D vector): fp32, shape (B, H, N), natural log
  *     of the scaled scores.
  *   - d must be 64 or 128; N >= 1; B, H >= 1; B*H*N*d < 2^40.
@@ -114,12 +115,49 @@ int fa_bwd_dq(const void* Q, const void* K, const void* V, const void* dO,
               const float* LSE, const float* Dvec, void* dQ,
               int B, int H, int N, int d, int causal, float scale, void* stream);
 
+/* Element type of the 16-bit tensors. */
+typedef enum {
+  FA_BF16 = 0,  /* bfloat16: what fa_fwd / fa_bwd take */
+  FA_F16 = 1    /* IEEE binary16 */
+} fa_dtype;
+
+/* Forward pass with the element type chosen by `dtype` (page 1, sections
+ * 1.2 and 6.3: the bias and the fix are described for FP16 and BF16 alike).  With FA_F16, Q, K, V and O
+ * are binary16, the products run on the f16 MFMA with FP32 accumulation, and
+ * the unnormalised probabilities are rounded to binary16 (to nearest even)
+ * before the product with V; everything else (FP32 scores, running maximum,
+ * row sum and shift rule) is as in fa_fwd.  row_shifted may be NULL; when
+ * given it is filled as by fa_fwd_diag.  FA_BF16 is fa_fwd / fa_fwd_diag.
+ * An unknown dtype returns FA_ERR_UNSUPPORTED. */
+int fa_fwd_ex(int dtype, const void* Q, const void* K, const void* V, void* O, float* LSE,
+              unsigned char* row_shifted,
+              int B, int H, int N, int d, int causal, float scale, int stabilize,
+              void* stream);
+
+/* Backward pass with the element type chosen by `dtype`: all eight 16-bit
+ * tensors are of that type, and P and dS are rounded to it (to nearest even)
+ * before their products.  Arguments, workspace and launches as in fa_bwd.
+ * FA_BF16 is fa_bwd.  An unknown dtype returns FA_ERR_UNSUPPORTED. */
+int fa_bwd_ex(int dtype, const void* Q, const void* K, const void* V, const void* O, const void* dO,
+              const float* LSE, void* dQ, void* dK, void* dV,
+              void* workspace, size_t workspace_bytes,
+              int B, int H, int N, int d, int causal, float scale, int stabilize,
+              void* stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* fa_status_string(int status);
 
 /* Constants of the stabilised shift rule, in base-2 exponent units
  * (reporting only; any pointer may be NULL). */
 void fa_stabilize_params(float* delta_min, float* delta_max, float* fold);
+
+/* The same constants for element type `dtype`.  For FA_F16 the largest
+ * probability 2^-delta must stay far inside binary16's exponent range (whose
+ * normal numbers end at 2^-14), so |R| is folded by whole units into (0, 1]:
+ * delta_max = fold = 1.  The folding moves the exponent by whole units only,
+ * so the rounding of the largest probability stays that of 2^-|R|.
+ * Returns FA_OK, or FA_ERR_UNSUPPORTED for an unknown dtype (nothing written). */
+int fa_stabilize_params_ex(int dtype, float* delta_min, float* delta_max, float* fold);
 
 /* Tile shape of the forward kernel for head dimension d (reporting only):
  * query rows and key columns per tile; 0 for unsupported d. */

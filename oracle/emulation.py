@@ -1,5 +1,5 @@
-"""Oracle B: BF16 blocked emulation of the tiled forward/backward
-(test infrastructure only).
+"""Oracle B: BF16 (or binary16) blocked emulation of the tiled
+forward/backward (test infrastructure only).
 
 It walks the one-pass tiled algorithm the pages describe -- blocks of keys,
 an online ("safe") softmax with running row maximum and running row sum
@@ -58,6 +58,14 @@ DELTA_MIN = 1.0 / 16.0   # base-2 exponent units
 DELTA_MAX = 64.0
 FOLD = 32.0
 
+# binary16: the largest probability 2^-delta must stay far inside binary16's
+# exponent range (normal numbers reach down to 2^-14 only), so |R| is folded
+# by whole units into (0, 1]
+F16_DELTA_MAX = 1.0
+F16_FOLD = 1.0
+
+RULES = {"bf16": (DELTA_MIN, DELTA_MAX, FOLD), "f16": (DELTA_MIN, F16_DELTA_MAX, F16_FOLD)}
+
 LOG2E = 1.4426950408889634
 LN2 = 0.6931471805599453
 
@@ -86,11 +94,26 @@ def bf16(x):
     return np.where(np.isnan(x32), np.nan, out)
 
 
-def _rounders(no_round: bool):
+def f16(x):
+    """Round to the nearest IEEE binary16 value, ties to even (returned as
+    float64): 11 significant bits, subnormals below 2^-14 with spacing 2^-24,
+    overflow to inf from 65520 up.  The rounding is numpy's float32 -> float16
+    conversion; the values rounded here are float32-exact, so going through
+    float32 first adds no second rounding.
+    """
+    with np.errstate(over="ignore"):
+        x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+        return x32.astype(np.float16).astype(np.float64)
+
+
+FORMATS = {"bf16": bf16, "f16": f16}
+
+
+def _rounders(no_round: bool, fmt: str = "bf16"):
     if no_round:
         ident = lambda x: np.asarray(x, dtype=np.float64)  # noqa: E731
         return ident, ident
-    return fl32, bf16
+    return fl32, FORMATS[fmt]
 
 
 # ----------------------------------------------------------------------------
@@ -98,31 +121,37 @@ def _rounders(no_round: bool):
 # ----------------------------------------------------------------------------
 
 def shift_rule(R: np.ndarray, tied: np.ndarray, stabilize: bool, delta_min: float,
-               delta_max: float, no_round: bool) -> np.ndarray:
+               delta_max: float, no_round: bool, fold: float = FOLD) -> np.ndarray:
     """Shift M (base-2 units) from the running maximum R = m*c and the tie flag."""
     r32, _ = _rounders(no_round)
     if not stabilize:
         return R.copy()
     a = np.abs(R)
     with np.errstate(invalid="ignore"):
-        over = np.where(a > delta_max, np.ceil((a - delta_max) / FOLD), 0.0)
-    a = a - FOLD * over                       # exact in fp32: whole multiples of 32
+        over = np.where(a > delta_max, np.ceil((a - delta_max) / fold), 0.0)
+    a = a - fold * over                       # exact in fp32: whole multiples of the fold
     delta = np.maximum(a, delta_min)
     shifted = r32(R + delta)
     return np.where(tied & np.isfinite(R), shifted, R)
 
 
 def forward(q, k, v, scale: float, causal: bool, *, block: int = 64, stabilize: bool,
-            no_round: bool = False, delta_min: float = DELTA_MIN, delta_max: float = DELTA_MAX,
-            return_state: bool = False):
+            no_round: bool = False, delta_min: Optional[float] = None, delta_max: Optional[float] = None,
+            return_state: bool = False, fmt: str = "bf16", fold: Optional[float] = None):
     """Blocked forward of one or more heads.
 
-    q, k, v: (..., N, d) arrays (bf16-exact values).  Returns (O, LSE) and,
+    q, k, v: (..., N, d) arrays (values exact in ``fmt``, the 16-bit element
+    type: "bf16", or "f16" for IEEE binary16, which replaces BF16 at every
+    16-bit rounding site).  Returns (O, LSE) and,
     with ``return_state``, a dict with the final running count, the final
     shift M, whether each row was ever shifted, and the largest probability
     that entered the PV product at a shifted step (for the "< 1" check).
     """
-    r32, rb16 = _rounders(no_round)
+    r32, rb16 = _rounders(no_round, fmt)
+    rule = RULES[fmt]
+    delta_min = rule[0] if delta_min is None else delta_min
+    delta_max = rule[1] if delta_max is None else delta_max
+    fold = rule[2] if fold is None else fold
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -161,7 +190,7 @@ def forward(q, k, v, scale: float, causal: bool, *, block: int = 64, stabilize: 
         m = np.maximum(m, bm)
         R = r32(m * c)
         tied = cnt >= 2
-        Mn = shift_rule(R, tied, stabilize, delta_min, delta_max, no_round)
+        Mn = shift_rule(R, tied, stabilize, delta_min, delta_max, no_round, fold)
         with np.errstate(invalid="ignore"):
             alpha = np.where(np.isfinite(Mn), r32(np.exp2(r32(M - Mn))), 1.0)
         p = r32(np.exp2(r32(t * c - Mn[..., None])))                # masked -> exp2(-inf) = 0
@@ -190,15 +219,17 @@ def forward(q, k, v, scale: float, causal: bool, *, block: int = 64, stabilize: 
 # backward
 # ----------------------------------------------------------------------------
 
-def backward(q, k, v, o, do, lse, scale: float, causal: bool, *, no_round: bool = False):
-    """Backward from the saved LSE, with the kernel's rounding sites.
+def backward(q, k, v, o, do, lse, scale: float, causal: bool, *, no_round: bool = False,
+             fmt: str = "bf16"):
+    """Backward from the saved LSE, with the kernel's rounding sites (16-bit
+    sites in ``fmt``, as in ``forward``).
 
     D = rowsum(dO * O) uses the bf16 forward output O.  P = 2^(t*c - LSE*log2 e)
     is recomputed in FP32 (the shift plays no part: P depends only on LSE);
     bf16(P) enters dV; dS = P (dP - D) is FP32 and is cast to bf16 before the
     dK and dQ products; the accumulators are FP32 and the results bf16.
     """
-    r32, rb16 = _rounders(no_round)
+    r32, rb16 = _rounders(no_round, fmt)
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)

@@ -61,6 +61,19 @@ def bf16_ulp(x) -> np.ndarray:
     return np.exp2(e - 7.0)
 
 
+def f16_ulp(x) -> np.ndarray:
+    """Spacing of binary16 numbers at |x| (11 significant bits): 2^(floor(log2|x|) - 10),
+    and 2^-24 in the subnormal range below 2^-14."""
+    ax = np.abs(_f64(x))
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    e = np.maximum(e, -14.0)
+    return np.exp2(e - 10.0)
+
+
+def ulp(x, fmt: str = "bf16") -> np.ndarray:
+    return f16_ulp(x) if fmt == "f16" else bf16_ulp(x)
+
+
 def _mean_se(x: np.ndarray):
     x = x.ravel()
     if x.size == 0:

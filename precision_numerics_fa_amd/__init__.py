@@ -1,4 +1,4 @@
-"""Tiled BF16 FlashAttention forward/backward for AMD MI355X (gfx950).
+"""Tiled BF16 (and FP16) FlashAttention forward/backward for AMD MI355X (gfx950).
 
 Thin Python binding of the C ABI in include/fa.h (libfa.so, built in-tree by
 ``python -m precision_numerics_fa_amd.build``).  PyTorch supplies device
@@ -10,16 +10,21 @@ not a gfx950 GPU, the calls raise.
     dq, dk, dv = bwd(q, k, v, o, do, lse, causal=True)
 
 Tensors are torch.bfloat16, shape (B, H, N, d), contiguous, on the current
-CUDA (HIP) device; LSE is float32 (B, H, N).
+CUDA (HIP) device; LSE is float32 (B, H, N).  fwd_ex / bwd_ex take
+torch.float16 tensors as well (the element type follows q).
 """
 from ._lib import (  # noqa: F401
+    FA_BF16,
+    FA_F16,
     FAError,
     bwd,
+    bwd_ex,
     bwd_dkdv,
     bwd_dot,
     bwd_dq,
     fwd,
     fwd_diag,
+    fwd_ex,
     fwd_tile,
     lib_path,
     load,

@@ -23,11 +23,18 @@ _SIGNATURES = {
     "fa_bwd_dot": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "fa_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
+    "fa_fwd_ex": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_ex": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_stabilize_params": (None, [ctypes.POINTER(_F)] * 3),
+    "fa_stabilize_params_ex": (_I, [_I] + [ctypes.POINTER(_F)] * 3),
     "fa_fwd_tile": (None, [_I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "fa_version": (_I, []),
 }
+
+
+FA_BF16 = 0
+FA_F16 = 1
 
 
 class FAError(RuntimeError):
@@ -67,9 +74,14 @@ def version() -> int:
     return int(load().fa_version())
 
 
-def stabilize_params() -> Tuple[float, float, float]:
+def stabilize_params(dtype: int = 0) -> Tuple[float, float, float]:
+    """(delta_min, delta_max, fold) of the shift rule for an element type
+    (FA_BF16 = 0, FA_F16 = 1)."""
     a, b, c = _F(), _F(), _F()
-    load().fa_stabilize_params(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    if dtype == 0:
+        load().fa_stabilize_params(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    else:
+        _call("fa_stabilize_params_ex", int(dtype), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
     return a.value, b.value, c.value
 
 
@@ -219,3 +231,54 @@ def bwd_dq(q, k, v, do, lse, dvec, causal: bool = False, scale: Optional[float] 
     _call("fa_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dvec), _ptr(dq),
           B, H, N, d, int(bool(causal)), _scale(scale, d), _stream())
     return dq
+
+
+# ---------------------------------------------------------------- element type chosen by the tensors
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float16:
+        return FA_F16
+    raise TypeError(f"q must be torch.bfloat16 or torch.float16, got {t.dtype}")
+
+
+def fwd_ex(q, k, v, causal: bool = False, scale: Optional[float] = None, stabilize: bool = False,
+           diag: bool = False):
+    """Forward pass in the element type of q (bfloat16 or float16).
+
+    Returns (O, LSE), plus the per-row shift report (uint8 (B,H,N)) when
+    ``diag``."""
+    torch = _torch()
+    B, H, N, d = _shape(q)
+    dev = q.device
+    code = _dtype_code(q)
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check(n, t, q.dtype, (B, H, N, d), dev)
+    o = torch.empty_like(q)
+    l = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    flags = torch.empty((B, H, N), dtype=torch.uint8, device=dev) if diag else None
+    _call("fa_fwd_ex", code, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), _ptr(flags) if diag else None,
+          B, H, N, d, int(bool(causal)), _scale(scale, d), int(bool(stabilize)), _stream())
+    return (o, l, flags) if diag else (o, l)
+
+
+def bwd_ex(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
+           stabilize: bool = False, workspace=None):
+    """Backward pass in the element type of q.  Returns (dQ, dK, dV)."""
+    torch = _torch()
+    B, H, N, d = _shape(q)
+    dev = q.device
+    code = _dtype_code(q)
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(n, t, q.dtype, (B, H, N, d), dev)
+    _check("lse", lse, torch.float32, (B, H, N), dev)
+    nbytes = workspace_bytes(B, H, N, d, causal)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _call("fa_bwd_ex", code, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+          _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, N, d,
+          int(bool(causal)), _scale(scale, d), int(bool(stabilize)), _stream())
+    return dq, dk, dv

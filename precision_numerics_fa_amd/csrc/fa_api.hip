@@ -45,15 +45,19 @@ int check_scale(float scale) { return (std::isfinite(scale) && scale > 0.0f) ? F
 
 int launched(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
 
-int fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, unsigned char* flags,
+int check_dtype(int dtype) { return (dtype == FA_BF16 || dtype == FA_F16) ? FA_OK : FA_ERR_UNSUPPORTED; }
+
+int fwd_impl(int dtype, const void* Q, const void* K, const void* V, void* O, float* LSE, unsigned char* flags,
              int B, int H, int N, int d, int causal, float scale, int stabilize, void* stream) {
-  int st = check_shape(B, H, N, d);
+  int st = check_dtype(dtype);
   if (st != FA_OK) return st;
+  if ((st = check_shape(B, H, N, d)) != FA_OK) return st;
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 4))
     return FA_ERR_INVALID_ARG;
   if ((st = check_scale(scale)) != FA_OK) return st;
   if ((st = check_device()) != FA_OK) return st;
-  fa::FwdArgs a{Q, K, V, O, LSE, flags, B, H, N, d, causal != 0, stabilize != 0, scale};
+  fa::FwdArgs a{Q, K, V, O, LSE, flags, B, H, N, d, causal != 0, stabilize != 0, scale,
+                dtype == FA_F16 ? fa::kF16 : fa::kBF16};
   (void)hipGetLastError();  // clear a stale error so a failure below is ours
   return launched(fa::launch_fwd(a, static_cast<hipStream_t>(stream)));
 }
@@ -68,19 +72,44 @@ int bwd_args(const void* Q, const void* K, const void* V, const void* dO, const 
   return check_scale(scale);
 }
 
+int bwd_impl(int dtype, const void* Q, const void* K, const void* V, const void* O, const void* dO,
+             const float* LSE, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, int B, int H,
+             int N, int d, int causal, float scale, int stabilize, void* stream) {
+  (void)stabilize;  // the backward recomputes P from LSE; the shift has no influence on it
+  int st = check_dtype(dtype);
+  if (st != FA_OK) return st;
+  if ((st = check_shape(B, H, N, d)) != FA_OK) return st;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(dO, 16) ||
+      !aligned(LSE, 4) || !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16))
+    return FA_ERR_INVALID_ARG;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (workspace == nullptr || !aligned(workspace, 4) ||
+      workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d, causal))
+    return FA_ERR_WORKSPACE;
+  if ((st = check_device()) != FA_OK) return st;
+  float* Dvec = static_cast<float*>(workspace);
+  fa::BwdArgs a{Q, K, V, O, dO, LSE, Dvec, dQ, dK, dV, B, H, N, d, causal != 0, scale,
+                dtype == FA_F16 ? fa::kF16 : fa::kBF16};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if ((st = launched(fa::launch_bwd_dot(a, s))) != FA_OK) return st;
+  if ((st = launched(fa::launch_bwd_dkdv(a, s))) != FA_OK) return st;
+  return launched(fa::launch_bwd_dq(a, s));
+}
+
 }  // namespace
 
 extern "C" {
 
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N, int d,
            int causal, float scale, int stabilize, void* stream) {
-  return fwd_impl(Q, K, V, O, LSE, nullptr, B, H, N, d, causal, scale, stabilize, stream);
+  return fwd_impl(FA_BF16, Q, K, V, O, LSE, nullptr, B, H, N, d, causal, scale, stabilize, stream);
 }
 
 int fa_fwd_diag(const void* Q, const void* K, const void* V, void* O, float* LSE, unsigned char* row_shifted,
                 int B, int H, int N, int d, int causal, float scale, int stabilize, void* stream) {
   if (row_shifted == nullptr) return FA_ERR_INVALID_ARG;
-  return fwd_impl(Q, K, V, O, LSE, row_shifted, B, H, N, d, causal, scale, stabilize, stream);
+  return fwd_impl(FA_BF16, Q, K, V, O, LSE, row_shifted, B, H, N, d, causal, scale, stabilize, stream);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int causal) {
@@ -133,23 +162,21 @@ int fa_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
            void* dK, void* dV, void* workspace, size_t workspace_bytes, int B, int H, int N, int d, int causal,
            float scale, int stabilize, void* stream) {
-  (void)stabilize;  // the backward recomputes P from LSE; the shift has no influence on it
-  int st = check_shape(B, H, N, d);
-  if (st != FA_OK) return st;
-  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(dO, 16) ||
-      !aligned(LSE, 4) || !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16))
-    return FA_ERR_INVALID_ARG;
-  if ((st = check_scale(scale)) != FA_OK) return st;
-  if (workspace == nullptr || !aligned(workspace, 4) || workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d, causal))
-    return FA_ERR_WORKSPACE;
-  if ((st = check_device()) != FA_OK) return st;
-  float* Dvec = static_cast<float*>(workspace);
-  fa::BwdArgs a{Q, K, V, O, dO, LSE, Dvec, dQ, dK, dV, B, H, N, d, causal != 0, scale};
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
-  if ((st = launched(fa::launch_bwd_dot(a, s))) != FA_OK) return st;
-  if ((st = launched(fa::launch_bwd_dkdv(a, s))) != FA_OK) return st;
-  return launched(fa::launch_bwd_dq(a, s));
+  return bwd_impl(FA_BF16, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, B, H, N, d, causal, scale,
+                  stabilize, stream);
+}
+
+int fa_fwd_ex(int dtype, const void* Q, const void* K, const void* V, void* O, float* LSE,
+              unsigned char* row_shifted, int B, int H, int N, int d, int causal, float scale, int stabilize,
+              void* stream) {
+  return fwd_impl(dtype, Q, K, V, O, LSE, row_shifted, B, H, N, d, causal, scale, stabilize, stream);
+}
+
+int fa_bwd_ex(int dtype, const void* Q, const void* K, const void* V, const void* O, const void* dO,
+              const float* LSE, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, int B, int H,
+              int N, int d, int causal, float scale, int stabilize, void* stream) {
+  return bwd_impl(dtype, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, B, H, N, d, causal, scale,
+                  stabilize, stream);
 }
 
 const char* fa_status_string(int status) {
@@ -170,12 +197,21 @@ void fa_stabilize_params(float* delta_min, float* delta_max, float* fold) {
   if (fold) *fold = fa::kFold;
 }
 
+int fa_stabilize_params_ex(int dtype, float* delta_min, float* delta_max, float* fold) {
+  if (check_dtype(dtype) != FA_OK) return FA_ERR_UNSUPPORTED;
+  const bool h = dtype == FA_F16;
+  if (delta_min) *delta_min = fa::kDeltaMin;
+  if (delta_max) *delta_max = h ? fa::kF16DeltaMax : fa::kDeltaMax;
+  if (fold) *fold = h ? fa::kF16Fold : fa::kFold;
+  return FA_OK;
+}
+
 void fa_fwd_tile(int d, int* block_q, int* block_k) {
   const bool ok = d == 64 || d == 128;
   if (block_q) *block_q = ok ? fa::kFwdBlockQ : 0;
   if (block_k) *block_k = ok ? fa::kFwdBlockK : 0;
 }
 
-int fa_version(void) { return 100; }
+int fa_version(void) { return 200; }
 
 }  // extern "C"

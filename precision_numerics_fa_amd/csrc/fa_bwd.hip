@@ -36,11 +36,16 @@
 namespace fa {
 namespace {
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// The low and high 16-bit values of a 32-bit word, widened to float.
+template <typename E>
+__device__ __forceinline__ float lo16(uint32_t w) { return widen16<E>(w & 0xFFFFu); }
+template <typename E>
+__device__ __forceinline__ float hi16(uint32_t w) { return widen16<E>(w >> 16); }
+template <>
+__device__ __forceinline__ float hi16<__bf16>(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // ---------------------------------------------------------------- D = rowsum(dO * O)
-template <int D>
+template <typename E, int D>
 __global__ __launch_bounds__(256) void bwd_dot_kernel(const bf16_t* __restrict__ O,
                                                       const bf16_t* __restrict__ dO,
                                                       float* __restrict__ Dvec, long long rows) {
@@ -52,9 +57,9 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const bf16_t* __restrict__
   if (row < rows) {
     const uint4 a = *reinterpret_cast<const uint4*>(O + row * D + c * 8);
     const uint4 b = *reinterpret_cast<const uint4*>(dO + row * D + c * 8);
-    acc = bf16_lo(a.x) * bf16_lo(b.x) + bf16_hi(a.x) * bf16_hi(b.x) + bf16_lo(a.y) * bf16_lo(b.y) +
-          bf16_hi(a.y) * bf16_hi(b.y) + bf16_lo(a.z) * bf16_lo(b.z) + bf16_hi(a.z) * bf16_hi(b.z) +
-          bf16_lo(a.w) * bf16_lo(b.w) + bf16_hi(a.w) * bf16_hi(b.w);
+    acc = lo16<E>(a.x) * lo16<E>(b.x) + hi16<E>(a.x) * hi16<E>(b.x) + lo16<E>(a.y) * lo16<E>(b.y) +
+          hi16<E>(a.y) * hi16<E>(b.y) + lo16<E>(a.z) * lo16<E>(b.z) + hi16<E>(a.z) * hi16<E>(b.z) +
+          lo16<E>(a.w) * lo16<E>(b.w) + hi16<E>(a.w) * hi16<E>(b.w);
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
@@ -75,15 +80,15 @@ __device__ __forceinline__ void load_rows_as_b(bf16x8* f, const bf16_t* rowp, bo
 
 // Write a transposed 32x32 accumulator set (rows = d, lane = one output row)
 // as bf16: element i of subtile t is column d = 32 t + 8 (i/4) + 4 hi + i%4.
-template <int D>
-__device__ __forceinline__ void store_row_bf16(bf16_t* rowp, const f32x16* acc, float mul, int hi) {
+template <typename E, int D>
+__device__ __forceinline__ void store_row(bf16_t* rowp, const f32x16* acc, float mul, int hi) {
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       uint2 w;
-      w.x = pack2(acc[t][4 * g + 0] * mul, acc[t][4 * g + 1] * mul);
-      w.y = pack2(acc[t][4 * g + 2] * mul, acc[t][4 * g + 3] * mul);
+      w.x = pack2<E>(acc[t][4 * g + 0] * mul, acc[t][4 * g + 1] * mul);
+      w.y = pack2<E>(acc[t][4 * g + 2] * mul, acc[t][4 * g + 3] * mul);
       *reinterpret_cast<uint2*>(rowp + t * 32 + g * 8 + 4 * hi) = w;
     }
 }
@@ -145,7 +150,7 @@ struct DkdvTile {
 // already B operands of dV^T = dO^T P and dK^T = Q^T dS, whose A operands
 // dO^T and Q^T come from the swizzled tiles through the transposing LDS read.
 // The register footprint allows two waves per SIMD.
-template <int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
@@ -237,8 +242,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     f32x16 sacc = zero16(), dacc = zero16();
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      sacc = mfma32x32x16(rd.row8(Qs, 0, kk), rd.row8(ktile, wave, kk), sacc);
-      dacc = mfma32x32x16(rd.row8(dOs, 0, kk), vf[kk], dacc);
+      sacc = mfma<E>(rd.row8(Qs, 0, kk), rd.row8(ktile, wave, kk), sacc);
+      dacc = mfma<E>(rd.row8(dOs, 0, kk), vf[kk], dacc);
     }
     // P = 2^(S c - LSE log2 e); the LDS copy of LSE is pre-scaled
 #pragma unroll
@@ -263,14 +268,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) dacc[4 * g + e] = sacc[4 * g + e] * (dacc[4 * g + e] - dv4[e]);
     }
-    const bf16x8 pb[2] = {pack8(sacc, 0), pack8(sacc, 8)};
-    const bf16x8 sb[2] = {pack8(dacc, 0), pack8(dacc, 8)};
+    const bf16x8 pb[2] = {pack8<E>(sacc, 0), pack8<E>(sacc, 8)};
+    const bf16x8 sb[2] = {pack8<E>(dacc, 0), pack8<E>(dacc, 8)};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        dv[dt] = mfma32x32x16(rd.col8(dOs, 0, ks, dt), pb[ks], dv[dt]);
-        dk[dt] = mfma32x32x16(rd.col8(Qs, 0, ks, dt), sb[ks], dk[dt]);
+        dv[dt] = mfma<E>(rd.col8(dOs, 0, ks, dt), pb[ks], dv[dt]);
+        dk[dt] = mfma<E>(rd.col8(Qs, 0, ks, dt), sb[ks], dk[dt]);
       }
   };
 
@@ -307,8 +312,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   for (; qb <= qb_last; ++qb) step(qb, std::false_type{});
 
   if (wave_live && myk < N) {
-    store_row_bf16<D>(dK + hoff + (size_t)myk * D, dk, scale, hi);
-    store_row_bf16<D>(dV + hoff + (size_t)myk * D, dv, 1.0f, hi);
+    store_row<E, D>(dK + hoff + (size_t)myk * D, dk, scale, hi);
+    store_row<E, D>(dV + hoff + (size_t)myk * D, dv, 1.0f, hi);
   }
 }
 
@@ -323,7 +328,7 @@ struct DqTile {
 };
 
 // ---------------------------------------------------------------- dQ
-template <int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
@@ -377,8 +382,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     dacc = zero16();
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      sacc = mfma32x32x16(rd.row8(Ks, sub, kk), qf[kk], sacc);
-      dacc = mfma32x32x16(rd.row8(Vs, sub, kk), dof[kk], dacc);
+      sacc = mfma<E>(rd.row8(Ks, sub, kk), qf[kk], sacc);
+      dacc = mfma<E>(rd.row8(Vs, sub, kk), dof[kk], dacc);
     }
   };
   // MASKED: the block may hold keys past N or (causal) after some query.
@@ -397,15 +402,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       if (MASKED && (i >> 2) * 8 + (i & 3) > lim) pv = 0.0f;
       ds[i] = pv * (dacc[i] - dq_d);
     }
-    sb[0] = pack8(ds, 0);
-    sb[1] = pack8(ds, 8);
+    sb[0] = pack8<E>(ds, 0);
+    sb[1] = pack8<E>(ds, 8);
   };
   // dQ^T += K^T dS^T for one subtile
   auto grads = [&](const TileReaderX<D>& rd, const bf16_t* Ks, int sub, const bf16x8* sb) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) dq[dt] = mfma32x32x16(rd.col8(Ks, sub, ks, dt), sb[ks], dq[dt]);
+      for (int dt = 0; dt < D / 32; ++dt) dq[dt] = mfma<E>(rd.col8(Ks, sub, ks, dt), sb[ks], dq[dt]);
   };
 
   load_tile_async<D, T::BS, T::NT>(ldoff, Kh, 0, N, ktile(0), wave, lane);
@@ -451,57 +456,72 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   for (; j < n_plain; ++j) step(j, std::false_type{});
   for (; j < n_kblk; ++j) step(j, std::true_type{});
 
-  if (wave_live && myq < N) store_row_bf16<D>(dQ + hoff + (size_t)myq * D, dq, scale, hi);
+  if (wave_live && myq < N) store_row<E, D>(dQ + hoff + (size_t)myq * D, dq, scale, hi);
 }
 
 inline int remap_ok(long long total) { return (total % 8 == 0) ? 1 : 0; }
 
-template <int D>
+template <typename E, int D>
 hipError_t launch_dot_t(const BwdArgs& a, hipStream_t s) {
   const long long rows = (long long)a.B * a.H * a.N;
   constexpr int RPB = 256 / (D / 8);
   const long long blocks = (rows + RPB - 1) / RPB;
-  hipLaunchKernelGGL((bwd_dot_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, s, (const bf16_t*)a.o,
+  hipLaunchKernelGGL((bwd_dot_kernel<E, D>), dim3((unsigned)blocks), dim3(256), 0, s, (const bf16_t*)a.o,
                      (const bf16_t*)a.dout, a.dvec, rows);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
   const int n_kblk = (a.N + DkdvTile<D>::B32 - 1) / DkdvTile<D>::B32;
   const long long total = (long long)a.B * a.H * n_kblk;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)total), dim3(256), 0, s,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL>), dim3((unsigned)total), dim3(256), 0, s,
                      (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.dout,
                      a.lse, a.dvec, (bf16_t*)a.dk, (bf16_t*)a.dv, a.N, n_kblk, (int)total,
                      remap_ok(total), scale_log2e(a.scale), a.scale);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL>
 hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
   const int n_qblk = (a.N + DqTile<D>::B32 - 1) / DqTile<D>::B32;
   const long long total = (long long)a.B * a.H * n_qblk;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)total), dim3(256), 0, s,
+  hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL>), dim3((unsigned)total), dim3(256), 0, s,
                      (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.dout,
                      a.lse, a.dvec, (bf16_t*)a.dq, a.N, n_qblk, (int)total, remap_ok(total),
                      scale_log2e(a.scale), a.scale);
   return hipGetLastError();
 }
 
+template <typename E>
+hipError_t dot_e(const BwdArgs& a, hipStream_t s) {
+  return a.d == 64 ? launch_dot_t<E, 64>(a, s) : launch_dot_t<E, 128>(a, s);
+}
+
+template <typename E>
+hipError_t dkdv_e(const BwdArgs& a, hipStream_t s) {
+  if (a.d == 64) return a.causal ? launch_dkdv_t<E, 64, true>(a, s) : launch_dkdv_t<E, 64, false>(a, s);
+  return a.causal ? launch_dkdv_t<E, 128, true>(a, s) : launch_dkdv_t<E, 128, false>(a, s);
+}
+
+template <typename E>
+hipError_t dq_e(const BwdArgs& a, hipStream_t s) {
+  if (a.d == 64) return a.causal ? launch_dq_t<E, 64, true>(a, s) : launch_dq_t<E, 64, false>(a, s);
+  return a.causal ? launch_dq_t<E, 128, true>(a, s) : launch_dq_t<E, 128, false>(a, s);
+}
+
 }  // namespace
 
 hipError_t launch_bwd_dot(const BwdArgs& a, hipStream_t s) {
-  return a.d == 64 ? launch_dot_t<64>(a, s) : launch_dot_t<128>(a, s);
+  return a.dtype == kF16 ? dot_e<_Float16>(a, s) : dot_e<__bf16>(a, s);
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s) {
-  if (a.d == 64) return a.causal ? launch_dkdv_t<64, true>(a, s) : launch_dkdv_t<64, false>(a, s);
-  return a.causal ? launch_dkdv_t<128, true>(a, s) : launch_dkdv_t<128, false>(a, s);
+  return a.dtype == kF16 ? dkdv_e<_Float16>(a, s) : dkdv_e<__bf16>(a, s);
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s) {
-  if (a.d == 64) return a.causal ? launch_dq_t<64, true>(a, s) : launch_dq_t<64, false>(a, s);
-  return a.causal ? launch_dq_t<128, true>(a, s) : launch_dq_t<128, false>(a, s);
+  return a.dtype == kF16 ? dq_e<_Float16>(a, s) : dq_e<__bf16>(a, s);
 }
 
 }  // namespace fa

@@ -1,9 +1,10 @@
 // Device-side building blocks shared by the forward and backward kernels:
-// vector types, the gfx950 bf16 MFMA, LDS loads (plain and transposing),
-// bf16 packing, and the repeated-maximum shift rule.
+// vector types, the gfx950 bf16 and f16 MFMAs, LDS loads (plain and
+// transposing), 16-bit packing, and the repeated-maximum shift rule.
 //
-// MFMA v_mfma_f32_32x32x16_bf16 operand layout (wave64, lane l, element j):
-//   A[m][k]: m = l % 32, k = 8 * (l / 32) + j      (8 bf16 per lane)
+// MFMA v_mfma_f32_32x32x16_{bf16,f16} operand layout (wave64, lane l,
+// element j):
+//   A[m][k]: m = l % 32, k = 8 * (l / 32) + j      (8 16-bit values per lane)
 //   B[k][n]: n = l % 32, k = 8 * (l / 32) + j
 //   C[r][n]: n = l % 32, r = 8 * (i / 4) + 4 * (l / 32) + (i % 4), i = 0..15
 // Both operands want the contraction index contiguous in a lane's registers.
@@ -34,15 +35,44 @@ constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// Shift-rule constants (base-2 exponent units).
+// Shift-rule constants (base-2 exponent units) for bf16.
 constexpr float kDeltaMin = 0.0625f;
 constexpr float kDeltaMax = 64.0f;
 constexpr float kFold = 32.0f;
+// For binary16 the largest probability 2^-delta must stay far inside its
+// exponent range (normal numbers end at 2^-14), so |R| is folded by whole
+// units into (0, 1].
+constexpr float kF16DeltaMax = 1.0f;
+constexpr float kF16Fold = 1.0f;
+
+template <typename E>
+struct ShiftRule {
+  static constexpr float dmin = kDeltaMin, dmax = kDeltaMax, fold = kFold;
+};
+template <>
+struct ShiftRule<_Float16> {
+  static constexpr float dmin = kDeltaMin, dmax = kF16DeltaMax, fold = kF16Fold;
+};
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Element types.  Tiles and MFMA operands hold 16-bit values as raw bits (a
+// bf16x8 register vector is eight 16-bit lanes, whatever their format); the
+// element type E, __bf16 or _Float16 (IEEE binary16), selects only the MFMA
+// instruction, the float -> 16-bit rounding (to nearest even) and the
+// 16-bit -> float widening.
+template <typename E>
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c);
+template <>
+__device__ __forceinline__ f32x16 mfma<__bf16>(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mfma<_Float16>(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                 0, 0);
 }
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -69,20 +99,36 @@ __device__ __forceinline__ bf16x8 join8(s16x4 lo, s16x4 hi) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Round-to-nearest-even float -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
-__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
-
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  __bf16 x = to_bf16(a), y = to_bf16(b);
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+// Round-to-nearest-even float -> 16-bit pattern of E (bf16: v_cvt_pk_bf16_f32
+// per pair on gfx950; binary16: v_cvt_f16_f32 per value).
+template <typename E>
+__device__ __forceinline__ uint16_t round16(float x) {
+  return __builtin_bit_cast(uint16_t, (E)x);
 }
 
-// Eight consecutive accumulator entries c[base .. base+7] as a bf16 MFMA operand.
+// Exact 16-bit pattern of E -> float.
+template <typename E>
+__device__ __forceinline__ float widen16(uint32_t h);
+template <>
+__device__ __forceinline__ float widen16<__bf16>(uint32_t h) { return __uint_as_float(h << 16); }
+template <>
+__device__ __forceinline__ float widen16<_Float16>(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+template <typename E>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return (uint32_t)round16<E>(a) | ((uint32_t)round16<E>(b) << 16);
+}
+
+// Eight consecutive accumulator entries c[base .. base+7] as an MFMA operand.
+template <typename E>
 __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int base) {
-  bf16x8 r;
+  typedef E e8 __attribute__((ext_vector_type(8)));
+  e8 r;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = to_bf16(c[base + j]);
-  return r;
+  for (int j = 0; j < 8; ++j) r[j] = (E)c[base + j];
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -227,22 +273,25 @@ __device__ __forceinline__ void zero_tail(int r0, int N, bf16_t* tile, int wave,
 }
 
 // The repeated-maximum shift (base-2 units).  R = running max * scale*log2e.
-// The shifted offset is R + delta with delta = max(|R|, kDeltaMin), |R|
-// folded by whole multiples of kFold into (kDeltaMax - kFold, kDeltaMax]
-// when larger than kDeltaMax.  Every step of delta is exact in fp32; delta is
-// finite for any R (a NaN from R = -inf is replaced by kDeltaMin).
+// The shifted offset is R + delta with delta = max(|R|, dmin), |R| folded by
+// whole multiples of `fold` into (dmax - fold, dmax] when larger than dmax
+// (the constants of ShiftRule<E>).  Every step of delta is exact in fp32;
+// delta is finite for any R (a NaN from R = -inf is replaced by dmin).
+template <typename E>
 __device__ __forceinline__ float shift_delta(float R) {
+  using C = ShiftRule<E>;
   const float a = __builtin_fabsf(R);
-  const float folded = a - kFold * __builtin_ceilf((a - kDeltaMax) * (1.0f / kFold));
-  const float d = a > kDeltaMax ? folded : a;
-  return __builtin_fmaxf(d, kDeltaMin);
+  const float folded = a - C::fold * __builtin_ceilf((a - C::dmax) * (1.0f / C::fold));
+  const float d = a > C::dmax ? folded : a;
+  return __builtin_fmaxf(d, C::dmin);
 }
 
 // Offset for a row: R + delta when the running maximum is tied, else R.
 // Written as R + delta * {0, 1} (exactly R or R + delta) so that it stays
 // branch-free inside the softmax basic block.
+template <typename E>
 __device__ __forceinline__ float row_offset(float R, bool tied) {
-  return R + shift_delta(R) * (tied ? 1.0f : 0.0f);
+  return R + shift_delta<E>(R) * (tied ? 1.0f : 0.0f);
 }
 
 }  // namespace fa

@@ -51,7 +51,7 @@ struct RowState {
   bool ever;   // the shift was applied at some block
 };
 
-template <int D, bool CAUSAL, bool STAB, bool DIAG>
+template <typename E, int D, bool CAUSAL, bool STAB, bool DIAG>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     bf16_t* __restrict__ O, float* __restrict__ LSE, uint8_t* __restrict__ row_shifted,
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
 #pragma unroll
       for (int t = 0; t < NS; ++t) {
         const char* base = reinterpret_cast<const char*>(Ks + t * 32 * D);
-        s[t] = mfma32x32x16(lds_load8(reinterpret_cast<const bf16_t*>(base + (kx ^ (uint32_t)(kk << 5)))), qf[kk],
+        s[t] = mfma<E>(lds_load8(reinterpret_cast<const bf16_t*>(base + (kx ^ (uint32_t)(kk << 5)))), qf[kk],
                             s[t]);
       }
   };
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
     const float R = m_new * c2;
     float Mn = R;
     if (STAB) {
-      Mn = row_offset(R, st.tied);
+      Mn = row_offset<E>(R, st.tied);
       if (DIAG) st.ever = st.ever || st.tied;
     }
     const float alpha = exp2_fast(st.M - Mn);  // 0 on the first block (M = -inf)
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) pb[ks] = pack8(s[ks >> 1], (ks & 1) * 8);
+    for (int ks = 0; ks < NK; ++ks) pb[ks] = pack8<E>(s[ks >> 1], (ks & 1) * 8);
   };
 
   // O^T += V^T bf16(P)^T for one block.
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
         const char* base = reinterpret_cast<const char*>(Vs + ks * 16 * D);
         const bf16x8 a = join8(lds_load_tr4(reinterpret_cast<const bf16_t*>(base + (va ^ (uint32_t)(dt << 6)))),
                                lds_load_tr4(reinterpret_cast<const bf16_t*>(base + (vb ^ (uint32_t)(dt << 6)))));
-        o[dt] = mfma32x32x16(a, pb[ks], o[dt]);
+        o[dt] = mfma<E>(a, pb[ks], o[dt]);
       }
   };
 
@@ -280,8 +280,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         uint2 w;
-        w.x = pack2(o[t][4 * g + 0] * rinv, o[t][4 * g + 1] * rinv);
-        w.y = pack2(o[t][4 * g + 2] * rinv, o[t][4 * g + 3] * rinv);
+        w.x = pack2<E>(o[t][4 * g + 0] * rinv, o[t][4 * g + 1] * rinv);
+        w.y = pack2<E>(o[t][4 * g + 2] * rinv, o[t][4 * g + 3] * rinv);
         *reinterpret_cast<uint2*>(Orow + t * 32 + g * 8 + 4 * hi) = w;
       }
     if (hi == 0) {
@@ -291,23 +291,29 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   }
 }
 
-template <int D, bool CAUSAL, bool STAB, bool DIAG>
+template <typename E, int D, bool CAUSAL, bool STAB, bool DIAG>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int n_qblk = (a.N + kFwdBlockQ - 1) / kFwdBlockQ;
   const long long total = (long long)a.B * a.H * n_qblk;
   const int remap = (total % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, STAB, DIAG>), dim3((unsigned)total), dim3(256), 0, stream,
+  hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, STAB, DIAG>), dim3((unsigned)total), dim3(256), 0, stream,
                      (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (bf16_t*)a.o, a.lse,
                      a.row_shifted, a.N, n_qblk, (int)total, remap, scale_log2e(a.scale));
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL>
 hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t s) {
   const bool diag = a.row_shifted != nullptr;
   if (a.stabilize)
-    return diag ? launch_fwd_t<D, CAUSAL, true, true>(a, s) : launch_fwd_t<D, CAUSAL, true, false>(a, s);
-  return diag ? launch_fwd_t<D, CAUSAL, false, true>(a, s) : launch_fwd_t<D, CAUSAL, false, false>(a, s);
+    return diag ? launch_fwd_t<E, D, CAUSAL, true, true>(a, s) : launch_fwd_t<E, D, CAUSAL, true, false>(a, s);
+  return diag ? launch_fwd_t<E, D, CAUSAL, false, true>(a, s) : launch_fwd_t<E, D, CAUSAL, false, false>(a, s);
+}
+
+template <typename E>
+hipError_t launch_fwd_e(const FwdArgs& a, hipStream_t s) {
+  if (a.d == 64) return a.causal ? launch_fwd_d<E, 64, true>(a, s) : launch_fwd_d<E, 64, false>(a, s);
+  return a.causal ? launch_fwd_d<E, 128, true>(a, s) : launch_fwd_d<E, 128, false>(a, s);
 }
 
 }  // namespace
@@ -315,8 +321,7 @@ hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t s) {
 float scale_log2e(float scale) { return (float)((double)scale * 1.4426950408889634); }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
-  if (a.d == 64) return a.causal ? launch_fwd_d<64, true>(a, s) : launch_fwd_d<64, false>(a, s);
-  return a.causal ? launch_fwd_d<128, true>(a, s) : launch_fwd_d<128, false>(a, s);
+  return a.dtype == kF16 ? launch_fwd_e<_Float16>(a, s) : launch_fwd_e<__bf16>(a, s);
 }
 
 }  // namespace fa

@@ -8,6 +8,10 @@
 
 namespace fa {
 
+// Element type of the 16-bit tensors (the values of fa_dtype in fa.h).
+constexpr int kBF16 = 0;
+constexpr int kF16 = 1;
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -19,6 +23,7 @@ struct FwdArgs {
   bool causal;
   bool stabilize;
   float scale;
+  int dtype;  // kBF16 or kF16
 };
 
 struct BwdArgs {
@@ -35,6 +40,7 @@ struct BwdArgs {
   int B, H, N, d;
   bool causal;
   float scale;
+  int dtype;  // kBF16 or kF16
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);

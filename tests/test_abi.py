@@ -44,6 +44,10 @@ def test_status_strings(lib):
 def test_stabilize_constants_match_the_oracle(lib):
     dmin, dmax, fold = fa.stabilize_params()
     assert (dmin, dmax, fold) == (EMU.DELTA_MIN, EMU.DELTA_MAX, EMU.FOLD)
+    assert fa.stabilize_params(fa.FA_BF16) == EMU.RULES["bf16"]
+    assert fa.stabilize_params(fa.FA_F16) == EMU.RULES["f16"]
+    x = ctypes.c_float(-7.0)
+    assert lib.fa_stabilize_params_ex(5, ctypes.byref(x), None, None) == -2 and x.value == -7.0
 
 
 def test_workspace_bytes(lib):
@@ -85,6 +89,22 @@ def test_backward_argument_validation(lib):
     assert lib.fa_bwd_dq(*[GOOD] * 6, GOOD, 1, 1, 8, 64, 1, -1.0, None) == -1
 
 
+def test_typed_entry_points_validate_dtype_and_arguments(lib):
+    """fa_fwd_ex / fa_bwd_ex: an unknown element type is FA_ERR_UNSUPPORTED,
+    and both known types go through the same argument checks as fa_fwd/fa_bwd."""
+    for bad in (-1, 2, 7):
+        assert lib.fa_fwd_ex(bad, GOOD, GOOD, GOOD, GOOD, GOOD, None, 1, 1, 64, 64, 0, 0.125, 0, None) == -2
+        need = fa.workspace_bytes(1, 1, 64, 64, False)
+        assert lib.fa_bwd_ex(bad, *[GOOD] * 10, need, 1, 1, 64, 64, 0, 0.125, 0, None) == -2
+    for dt in (fa.FA_BF16, fa.FA_F16):
+        assert lib.fa_fwd_ex(dt, None, GOOD, GOOD, GOOD, GOOD, None, 1, 1, 64, 64, 0, 0.125, 0, None) == -1
+        assert lib.fa_fwd_ex(dt, GOOD, GOOD, GOOD, GOOD, GOOD, None, 1, 1, 64, 96, 0, 0.125, 0, None) == -2
+        assert lib.fa_fwd_ex(dt, GOOD, GOOD, GOOD, GOOD, GOOD, None, 1, 1, 64, 64, 0, 0.0, 0, None) == -1
+        need = fa.workspace_bytes(2, 2, 100, 64, True)
+        assert lib.fa_bwd_ex(dt, *[GOOD] * 9, GOOD, need - 4, 2, 2, 100, 64, 1, 0.125, 0, None) == -3
+        assert lib.fa_bwd_ex(dt, *[GOOD] * 8, P(4098), GOOD, need, 2, 2, 100, 64, 1, 0.125, 0, None) == -1
+
+
 def test_no_gpu_means_an_error_not_a_fallback(lib):
     """Valid arguments on a host without a gfx950 GPU: FA_ERR_DEVICE."""
     import torch
@@ -93,3 +113,6 @@ def test_no_gpu_means_an_error_not_a_fallback(lib):
     assert _fwd(lib) == -5
     need = fa.workspace_bytes(1, 1, 64, 64, False)
     assert lib.fa_bwd(*[GOOD] * 9, GOOD, need, 1, 1, 64, 64, 0, 0.125, 0, None) == -5
+    for dt in (fa.FA_BF16, fa.FA_F16):
+        assert lib.fa_fwd_ex(dt, GOOD, GOOD, GOOD, GOOD, GOOD, None, 1, 1, 64, 64, 0, 0.125, 0, None) == -5
+        assert lib.fa_bwd_ex(dt, *[GOOD] * 10, need, 1, 1, 64, 64, 0, 0.125, 0, None) == -5

@@ -1,0 +1,216 @@
+"""GPU parity of the binary16 path (fa_fwd_ex / fa_bwd_ex with FA_F16, through
+the C ABI) against the CPU oracle.
+
+Page 1 (sections 1.2 and 6.3) describes the bias and the fix for FP16 and
+BF16 alike.  Gates, derived from the arithmetic: binary16 keeps 3 more
+significant bits than bf16 at every 16-bit rounding site, so the bf16 gates
+(1.5e-2 max, 2e-3 mean |dO|) scale to about 1.9e-3 and 2.5e-4; with a margin
+of two for the GPU's own summation order and exp2 this gives 4e-3 and 4e-4.
+The blocked binary16 emulation's worst case over the small shapes below is
+1.1e-3 / 8.8e-5.  Gradients: relative Frobenius error <= 1e-2 (emulation:
+3e-4).  Where |O| reaches 4 (the Q,K x4 workload) one binary16 ulp of O
+(2^-8) is also allowed.
+"""
+import numpy as np
+import pytest
+
+import fa_inputs as F
+from oracle import emulation as EMU
+from oracle import metrics as Mt
+from oracle import reference as REF
+
+from gpu_util import device_inputs, head_f64, random_case, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 4e-3
+MEAN_ABS = 4e-4
+GRAD_REL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+    import precision_numerics_fa_amd as fa
+    assert torch.cuda.is_available()
+    fa.load()
+    return fa
+
+
+def _gate_o(o_gpu, o_ref, loose_format=False):
+    e = Mt.output_errors(o_gpu, o_ref)
+    d = np.abs(o_gpu - o_ref)
+    if loose_format:
+        bound = np.maximum(MAX_ABS, Mt.f16_ulp(o_ref))
+        assert (d <= bound).all(), f"worst |dO|/bound = {(d / bound).max():.3f}"
+    else:
+        assert e["max_abs"] <= MAX_ABS, e
+    assert e["mean_abs"] <= MEAN_ABS, e
+    assert e["finite"]
+    return e
+
+
+SMALL = [(1, 1, 1, 64), (1, 2, 17, 64), (2, 3, 128, 64), (1, 2, 200, 128), (2, 1, 333, 128),
+         (1, 1, 129, 128), (3, 1, 257, 64)]
+
+
+@pytest.mark.parametrize("stabilize", [False, True])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N,d", SMALL)
+def test_f16_fwd_small_against_oracle(fa, B, H, N, d, causal, stabilize):
+    import torch
+    say(f"f16 fwd small B={B} H={H} N={N} d={d} causal={causal} stabilize={stabilize}")
+    bits, dev = random_case(B, H, N, d, seed=N * 7 + d + B, dtype="f16")
+    assert dev["q"].dtype == torch.float16
+    o, lse = fa.fwd_ex(dev["q"], dev["k"], dev["v"], causal=causal, stabilize=stabilize)
+    assert o.dtype == torch.float16
+    q, k, v = (head_f64(bits[n], "f16") for n in ("q", "k", "v"))
+    o_ref, lse_ref = REF.forward(q, k, v, 1.0 / np.sqrt(d), causal)
+    _gate_o(to_f64(o), o_ref)
+    assert np.abs(to_f64(lse) - lse_ref).max() <= 1e-4
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N,d", [(1, 2, 17, 64), (2, 1, 200, 128), (1, 3, 130, 64), (1, 1, 1, 128)])
+def test_f16_bwd_small_against_oracle(fa, B, H, N, d, causal):
+    say(f"f16 bwd small B={B} H={H} N={N} d={d} causal={causal}")
+    bits, dev = random_case(B, H, N, d, seed=N * 3 + d, with_do=True, dtype="f16")
+    scale = 1.0 / np.sqrt(d)
+    o, lse = fa.fwd_ex(dev["q"], dev["k"], dev["v"], causal=causal, stabilize=True)
+    dq, dk, dv = fa.bwd_ex(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=causal)
+    q, k, v, do = (head_f64(bits[n], "f16") for n in ("q", "k", "v", "do"))
+    rq, rk, rv = REF.backward(q, k, v, do, scale, causal)
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        g = to_f64(g)
+        if not np.any(r):
+            # an exactly zero gradient (N = 1: P = 1, so dS = dP - D = 0): the
+            # GPU's dP and D round in different orders, leaving |dS| at the
+            # fp32 rounding level of |dO.V| (~1e-6), scaled into dQ by K
+            assert np.abs(g).max() <= 1e-4, (name, np.abs(g).max())
+            continue
+        rel = Mt.relative_fro(g, r)
+        assert rel <= GRAD_REL, (name, rel)
+
+
+def test_f16_close_to_emulation(fa):
+    """Against the binary16 emulation: most outputs agree to the bit.  The rest
+    differ where the GPU's exp2 or summation order flips the binary16 rounding
+    of one probability, which moves O by up to about 2^-11 * P_k/l * |v_k|:
+    a few binary16 ulps at the row's scale (max |O| of the row), though many
+    ulps of an entry that happens to be near zero."""
+    w = F.WORKLOADS["c1"].with_shape(dtype="f16")
+    full, dev = device_inputs(w)
+    q, k, v = (head_f64(full[n][0, 0], "f16") for n in ("q", "k", "v"))
+    for stab in (False, True):
+        o, _ = fa.fwd_ex(dev["q"], dev["k"], dev["v"], causal=False, stabilize=stab)
+        ob, _ = EMU.forward(q, k, v, w.scale, False, block=fa.fwd_tile(64)[1], stabilize=stab, fmt="f16")
+        of = to_f64(o[0, 0])
+        same = (of == ob).mean()
+        row_scale = np.abs(ob).max(axis=-1, keepdims=True)
+        ulps = np.abs(of - ob) / Mt.f16_ulp(row_scale)
+        say(f"  f16 emulation agreement stabilize={stab}: identical {same:.3f}, "
+            f"max ulps at row scale {ulps.max():.2f}")
+        assert same > 0.9 and ulps.max() <= 4
+
+
+def test_f16_fix_touches_only_rows_with_a_repeated_maximum(fa):
+    import torch
+    say("f16 invariant: fix only on tie rows")
+    w = F.WORKLOADS["c2h"].with_shape(B=2, H=3)
+    full, dev = device_inputs(w)
+    o0, l0, f0 = fa.fwd_ex(dev["q"], dev["k"], dev["v"], causal=True, stabilize=False, diag=True)
+    o1, l1, f1 = fa.fwd_ex(dev["q"], dev["k"], dev["v"], causal=True, stabilize=True, diag=True)
+    assert int(f0.sum()) == 0
+    never = (f1 == 0)
+    assert torch.equal(o0[never], o1[never]) and torch.equal(l0[never], l1[never])
+    f1n = f1.cpu().numpy()
+    for (b, h), rows in full["tie_rows"].items():
+        assert (f1n[b, h, rows] == 1).all()
+
+
+def test_c2h_full_and_tie_bias(fa):
+    """Binary16, Q,K x4, causal, 5% repeated-max rows, all 96 heads: the
+    aligned signed error on tie rows is positive with the fix off and drops
+    with it on (emulation: +5.0e-6 -> +0.6e-6, about 12 times smaller than in
+    bf16, as 3 more significant bits predict)."""
+    w = F.WORKLOADS["c2h"]
+    full, dev = device_inputs(w)
+    res = {}
+    for stabilize in (False, True):
+        say(f"c2h stabilize={stabilize}")
+        o, lse = fa.fwd_ex(dev["q"], dev["k"], dev["v"], causal=True, stabilize=stabilize)
+        of, lf = to_f64(o), to_f64(lse)
+        stats = []
+        for b in range(w.B):
+            q, k, v = (head_f64(full[n][b], "f16") for n in ("q", "k", "v"))
+            o_ref, lse_ref = REF.forward(q, k, v, w.scale, True)
+            _gate_o(of[b], o_ref, loose_format=True)
+            assert np.abs(lf[b] - lse_ref).max() <= 1e-4
+            meta = REF.tie_metadata(q, k, v, w.scale, True)
+            stats.append((of[b] - o_ref, np.sign(o_ref - meta["tie_mean"]), meta["count"] >= 2))
+        d = np.concatenate([s[0][s[2]] for s in stats])
+        sg = np.concatenate([s[1][s[2]] for s in stats])
+        aligned = (d * sg).mean()
+        se = (d * sg).std(ddof=1) / np.sqrt(d.size)
+        res[stabilize] = (aligned, se)
+        say(f"  c2h stabilize={stabilize} tie rows aligned signed error {aligned:+.3e} +- {se:.1e}, "
+            f"plain {d.mean():+.3e}")
+    assert res[False][0] > 4 * res[False][1]
+    assert abs(res[True][0]) < 0.5 * res[False][0]
+
+
+@pytest.mark.parametrize("stabilize", [False, True])
+def test_c4h_full_sampled_heads(fa, stabilize):
+    w = F.WORKLOADS["c4h"]
+    say(f"c4h stabilize={stabilize} (full size, 8 sampled heads)")
+    full, dev = device_inputs(w)
+    o, lse = fa.fwd_ex(dev["q"], dev["k"], dev["v"], causal=True, stabilize=stabilize)
+    worst = 0.0
+    for (b, h) in F.sample_pairs(w, 8):
+        q, k, v = (head_f64(full[n][b, h], "f16") for n in ("q", "k", "v"))
+        o_ref, lse_ref = REF.forward(q, k, v, w.scale, True)
+        e = _gate_o(to_f64(o[b, h]), o_ref)
+        worst = max(worst, e["max_rel_normwise"])
+        assert np.abs(lse[b, h].cpu().numpy() - lse_ref).max() <= 1e-4
+    say(f"  c4h stabilize={stabilize} max relative error (normwise) {worst:.3e}")
+
+
+def test_c5h_full_forward_backward_sampled_heads(fa):
+    w = F.WORKLOADS["c5h"]
+    say("c5h forward+backward (full size, 16 sampled heads)")
+    full, dev = device_inputs(w)
+    o, lse = fa.fwd_ex(dev["q"], dev["k"], dev["v"], causal=True, stabilize=True)
+    dq, dk, dv = fa.bwd_ex(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=True)
+    worst = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    for (b, h) in F.sample_pairs(w, 16):
+        q, k, v, do = (head_f64(full[n][b, h], "f16") for n in ("q", "k", "v", "do"))
+        o_ref, _ = REF.forward(q, k, v, w.scale, True)
+        _gate_o(to_f64(o[b, h]), o_ref)
+        rq, rk, rv = REF.backward(q, k, v, do, w.scale, True)
+        for name, g, r in (("dq", dq[b, h], rq), ("dk", dk[b, h], rk), ("dv", dv[b, h], rv)):
+            rel = Mt.relative_fro(to_f64(g), r)
+            worst[name] = max(worst[name], rel)
+            assert rel <= GRAD_REL, (name, b, h, rel)
+    say("  c5h worst relative gradient errors", worst)
+
+
+def test_f16_is_closer_to_exact_than_bf16(fa):
+    """The element type changes only the 16-bit rounding sites: on the same
+    inputs (the bf16 draws, converted to binary16), the binary16 result is
+    several times closer to the exact oracle than the bf16 one."""
+    import torch
+    w = F.WORKLOADS["c5"].with_shape(B=1, H=4)
+    full, dev = device_inputs(w)
+    o_b, _ = fa.fwd(dev["q"], dev["k"], dev["v"], causal=True, stabilize=True)
+    qh, kh, vh = (dev[n].to(torch.float16) for n in ("q", "k", "v"))
+    o_h, _ = fa.fwd_ex(qh, kh, vh, causal=True, stabilize=True)
+    eb = eh = 0.0
+    for h in range(w.H):
+        q, k, v = (head_f64(full[n][0, h]) for n in ("q", "k", "v"))
+        o_ref, _ = REF.forward(q, k, v, w.scale, True)
+        eb += np.abs(to_f64(o_b[0, h]) - o_ref).mean()
+        qf, kf, vf = (x[0, h].double().cpu().numpy() for x in (qh, kh, vh))
+        o_ref_h, _ = REF.forward(qf, kf, vf, w.scale, True)
+        eh += np.abs(to_f64(o_h[0, h]) - o_ref_h).mean()
+    say(f"  mean |dO| bf16 {eb / w.H:.3e}  f16 {eh / w.H:.3e}")
+    assert eh < eb / 4

@@ -83,7 +83,14 @@ def test_bwd_small_against_oracle(fa, B, H, N, d, causal):
     q, k, v, do = (head_f64(bits[n]) for n in ("q", "k", "v", "do"))
     rq, rk, rv = REF.backward(q, k, v, do, scale, causal)
     for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
-        rel = Mt.relative_fro(to_f64(g), r)
+        g = to_f64(g)
+        if not np.any(r):
+            # an exactly zero gradient (N = 1: P = 1, so dS = dP - D = 0): the
+            # GPU's dP and D round in different orders, leaving |dS| at the
+            # fp32 rounding level of |dO.V| (~1e-6), scaled into dQ by K
+            assert np.abs(g).max() <= 1e-4, (name, np.abs(g).max())
+            continue
+        rel = Mt.relative_fro(g, r)
         assert rel <= GRAD_REL, (name, rel)
 
 

@@ -13,7 +13,12 @@
   bfloat16 conversion (round to nearest even).
 * A hand-derived worked example (tests/golden/tie_midpoint.json) pins the
   rounding sites: the bf16 cast of P before the PV product, the unrounded row
-  sum and the bf16 output cast.
+  sum and the bf16 output cast; tie_midpoint_f16.json pins the same sites in
+  binary16.
+* The binary16 rounding is checked against PyTorch's float32 -> float16
+  conversion and hand-computed ties, subnormals and overflow, and the
+  binary16 emulation must be closer to the exact result than the bf16 one on
+  the same (bf16-exact) inputs.
 """
 import json
 import math
@@ -34,7 +39,7 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 def _head(name, b=0, h=0, **kw):
     w = F.WORKLOADS[name].with_shape(**kw) if kw else F.WORKLOADS[name]
     hd = F.head(w, b, h)
-    return w, [F.bf16_bits_to_f32(hd[n]).astype(np.float64) for n in ("q", "k", "v")], hd
+    return w, [F.decode(hd[n], w.dtype).astype(np.float64) for n in ("q", "k", "v")], hd
 
 
 # ---------------------------------------------------------------- primitives
@@ -50,6 +55,35 @@ def test_bf16_matches_torch_round_to_nearest_even():
     ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(mine, ref)
     assert np.isnan(B.bf16(np.array([np.nan]))).all()
+
+
+def test_f16_matches_torch_and_hand_values():
+    rng = np.random.default_rng(6)
+    x = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 6, 20000),
+        [0.0, -0.0, 1.0, 65504.0, 70000.0, -70000.0, 1e-8, -3e-8, 0.1353352814912796],
+    ]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float16).to(torch.float64).numpy()
+    assert np.array_equal(B.f16(x), ref)
+    hand = {
+        1.0 + 2.0 ** -11: 1.0,                       # tie: to the even neighbour 1.0
+        1.0 + 3 * 2.0 ** -11: 1.0 + 2.0 ** -9,       # tie: to the even neighbour above
+        1.0 + 2.0 ** -11 + 2.0 ** -20: 1.0 + 2.0 ** -10,
+        65519.0: 65504.0,                            # below the overflow midpoint
+        65520.0: np.inf,                             # the midpoint rounds to inf
+        2.0 ** -25: 0.0,                             # half the smallest subnormal: to even (0)
+        3 * 2.0 ** -26: 2.0 ** -24,
+        2.0 ** -14 + 2.0 ** -25: 2.0 ** -14,         # subnormal-range spacing is 2^-24
+    }
+    for a, b in hand.items():
+        assert B.f16(np.array([a]))[0] == b, (a, b)
+    assert np.isnan(B.f16(np.array([np.nan]))).all()
+
+
+def test_ulp_helpers():
+    assert Mt.f16_ulp(np.array([1.0, 1.5, 0.5, 2.0 ** -20, 65504.0])).tolist() == \
+        [2.0 ** -10, 2.0 ** -10, 2.0 ** -11, 2.0 ** -24, 32.0]
+    assert Mt.bf16_ulp(np.array([1.0, 3.0])).tolist() == [2.0 ** -7, 2.0 ** -6]
 
 
 def test_fl32_is_float32_rounding():
@@ -147,6 +181,34 @@ def test_rounded_emulation_within_tolerance_c1(stabilize):
     assert np.abs(lb - lse).max() <= 1e-5
 
 
+def test_binary16_emulation_is_closer_than_bf16():
+    """The binary16 rounding sites have 3 more significant bits than bf16, so on
+    the same inputs (bf16 values, exact in binary16 here) the emulated output
+    error against the exact oracle shrinks by about 2^3."""
+    w, (q, k, v), _ = _head("c1")
+    assert np.array_equal(B.f16(q), q) and np.array_equal(B.f16(k), k) and np.array_equal(B.f16(v), v)
+    o, _ = A.forward(q, k, v, w.scale, w.causal)
+    for stab in (False, True):
+        eb = np.abs(B.forward(q, k, v, w.scale, False, block=64, stabilize=stab)[0] - o).mean()
+        eh = np.abs(B.forward(q, k, v, w.scale, False, block=64, stabilize=stab, fmt="f16")[0] - o).mean()
+        assert eh < eb / 4, (stab, eh, eb)
+        assert eh > eb / 32, (stab, eh, eb)
+
+
+def test_rounded_f16_emulation_within_tolerance():
+    w, (q, k, v), hd = _head("c5h", N=256)
+    assert w.dtype == "f16"
+    do = F.decode(hd["do"], "f16").astype(np.float64)
+    o, lse = A.forward(q, k, v, w.scale, True)
+    ob, lb = B.forward(q, k, v, w.scale, True, block=64, stabilize=True, fmt="f16")
+    e = Mt.output_errors(ob, o)
+    assert e["max_abs"] <= 2e-3 and e["mean_abs"] <= 2.5e-4
+    dq, dk, dv = A.backward(q, k, v, do, w.scale, True)
+    eq, ek, ev = B.backward(q, k, v, ob, do, lb, w.scale, True, fmt="f16")
+    for a, b in ((eq, dq), (ek, dk), (ev, dv)):
+        assert Mt.relative_fro(a, b) <= 1e-2
+
+
 def test_rounded_backward_within_tolerance():
     w, (q, k, v), _ = _head("c5", N=256)
     do = F.bf16_bits_to_f32(F.head(F.WORKLOADS["c5"].with_shape(N=256), 0, 0)["do"]).astype(np.float64)
@@ -180,3 +242,35 @@ def test_hand_worked_tie_midpoint():
     fq, fk = np.array(g["fold_q"]), np.array(g["fold_k"])
     _, _, st = B.forward(fq, fk, v, g["scale"], False, block=64, stabilize=True, return_state=True)
     assert st["shift"][0] == np.float32(g["fold_R"] + g["fold_delta"])
+
+
+def test_hand_worked_tie_midpoint_f16():
+    g = json.load(open(os.path.join(GOLDEN, "tie_midpoint_f16.json")))
+    q, k, v = (np.array(g[n], dtype=np.float64) for n in ("q", "k", "v"))
+    o_off, lse_off = B.forward(q, k, v, g["scale"], False, block=64, stabilize=False, fmt="f16")
+    o_on, lse_on, st = B.forward(q, k, v, g["scale"], False, block=64, stabilize=True, return_state=True,
+                                 fmt="f16")
+    assert A.forward(q, k, v, g["scale"], False)[0][0, 0] == g["o_exact"]
+    assert o_off[0, 0] == g["o_fix_off"]
+    assert o_on[0, 0] == g["o_fix_on"]
+    assert st["pmax_shifted_bf16"][0] == g["p_fix_on_f16"]
+    assert abs(lse_off[0] - g["lse"]) <= 1e-6 and abs(lse_on[0] - g["lse"]) <= 1e-6
+
+
+def test_binary16_rule_keeps_the_largest_probability_representable():
+    """Why binary16 has its own fold.  With the bf16 constants (|R| up to 64)
+    the largest probability 2^-|R| of a shifted row underflows in binary16 once
+    |R| > 24 and the row's output is lost; folding |R| into (0, 1] keeps it in
+    [1/2, 1) and the output within tolerance."""
+    w, (q, k, v), _ = _head("c2h", N=512)
+    o, _ = A.forward(q, k, v, w.scale, True)
+    ob, _, st = B.forward(q, k, v, w.scale, True, stabilize=True, fmt="f16", return_state=True)
+    shifted = st["ever_shifted"]
+    assert shifted.sum() >= 10
+    pm = st["pmax_shifted_bf16"][shifted]
+    assert (pm >= 0.5).all() and (pm < 1.0).all()
+    assert np.abs(ob - o).max() <= 2e-2
+    bad, _, st2 = B.forward(q, k, v, w.scale, True, stabilize=True, fmt="f16", return_state=True,
+                            delta_max=B.DELTA_MAX, fold=B.FOLD)
+    assert (st2["pmax_shifted_bf16"][shifted] == 0.0).any()
+    assert np.abs(bad - o).max() > 0.1
