@@ -222,9 +222,37 @@ def main():
         "input_gen_s": round(gen_s, 2),
     }
 
+    out["f16"] = f16_leg(args, fwd_flop, bwd_flop)
     if not args.no_cpu_baseline:
         out.update(cpu_baseline_leg(w, full, o, lse, dq, dk, dv, args.cpu_heads, fwd_flop + bwd_flop))
     print(json.dumps(out), flush=True)
+
+
+def f16_leg(args, fwd_flop, bwd_flop):
+    """The same shape in IEEE binary16 (fa_fwd_ex / fa_bwd_ex): forward with
+    the fix on, and the whole backward, each timed alone with HIP events."""
+    import numpy as np
+    import torch
+
+    import fa_inputs as F
+    import precision_numerics_fa_amd as fa
+
+    w = F.WORKLOADS["c4h"].with_shape(with_do=True)
+    full = F.full(w)
+    q, k, v, do = (torch.from_numpy(full[n].view(np.int16)).view(torch.float16).cuda()
+                   for n in ("q", "k", "v", "do"))
+    del full
+    res = {}
+    fwd = lambda: res.update(zip("ol", fa.fwd_ex(q, k, v, causal=True, stabilize=True)))
+    t_fwd = _timed(fwd, args.steps)
+    fwd()
+    t_bwd = _timed(lambda: fa.bwd_ex(q, k, v, res["o"], do, res["l"], causal=True), args.steps)
+    del q, k, v, do, res
+    torch.cuda.empty_cache()
+    return {"workload": "same shape, IEEE binary16 inputs and rounding sites",
+            "fwd_ms": round(t_fwd, 4), "fwd_tflops": round(fwd_flop / (t_fwd * 1e-3) / 1e12, 1),
+            "fwd_pct_peak": round(100 * fwd_flop / (t_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "bwd_ms": round(t_bwd, 4), "bwd_tflops": round(bwd_flop / (t_bwd * 1e-3) / 1e12, 1)}
 
 
 def _timed(fn, reps):
@@ -254,27 +282,35 @@ def sweep(args):
         w = w0.with_shape(with_do=True)
         B, H, N, d = w.B, w.H, w.N, w.d
         full = F.full(w)
-        dev = {n: torch.from_numpy(full[n].view(np.int16)).view(torch.bfloat16).cuda()
-               for n in ("q", "k", "v", "do")}
+        tdt = torch.float16 if w.dtype == "f16" else torch.bfloat16
+        dev = {n: torch.from_numpy(full[n].view(np.int16)).view(tdt).cuda() for n in ("q", "k", "v", "do")}
         del full
         q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
-        o = torch.empty_like(q)
-        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
         reps = args.steps
-        fon = lambda: fa.fwd(q, k, v, causal=w.causal, stabilize=True, out=o, lse=lse)
-        foff = lambda: fa.fwd(q, k, v, causal=w.causal, stabilize=False, out=o, lse=lse)
+        res = {}
+        if w.dtype == "f16":
+            fon = lambda: res.update(zip("ol", fa.fwd_ex(q, k, v, causal=w.causal, stabilize=True)))
+            foff = lambda: res.update(zip("ol", fa.fwd_ex(q, k, v, causal=w.causal, stabilize=False)))
+            bwd = lambda: fa.bwd_ex(q, k, v, res["o"], do, res["l"], causal=w.causal)
+        else:
+            o = torch.empty_like(q)
+            lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+            res.update(o=o, l=lse)
+            fon = lambda: fa.fwd(q, k, v, causal=w.causal, stabilize=True, out=o, lse=lse)
+            foff = lambda: fa.fwd(q, k, v, causal=w.causal, stabilize=False, out=o, lse=lse)
+            bwd = lambda: fa.bwd(q, k, v, o, do, lse, causal=w.causal)
         _timed(fon, 4 * reps)  # clocks up
         # fix on and off alternate; the fastest of three rounds each
         t_on = min(_timed(fon, reps) for _ in range(3))
         t_off = min(_timed(foff, reps) for _ in range(3))
         t_on = min(t_on, *(_timed(fon, reps) for _ in range(2)))
         fon()
-        t_bwd = min(_timed(lambda: fa.bwd(q, k, v, o, do, lse, causal=w.causal), reps) for _ in range(3))
+        t_bwd = min(_timed(bwd, reps) for _ in range(3))
         pairs = N * (N + 1) / 2 if w.causal else N * N
         fwd_flop = 4.0 * B * H * pairs * d
         elem = B * H * N * d
         fwd_bytes = 4 * elem * 2 + B * H * N * 4
-        rec = {"workload": name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+        rec = {"workload": name, "dtype": w.dtype, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
                "fwd_stab_ms": round(t_on, 4), "fwd_plain_ms": round(t_off, 4),
                "fwd_tflops": round(fwd_flop / (t_on * 1e-3) / 1e12, 1),
                "fwd_pct_peak": round(100 * fwd_flop / (t_on * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
@@ -284,7 +320,7 @@ def sweep(args):
                "bwd_tflops": round(2.5 * fwd_flop / (t_bwd * 1e-3) / 1e12, 1),
                "bwd_pct_peak": round(100 * 2.5 * fwd_flop / (t_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
         print(json.dumps(rec), flush=True)
-        del dev, q, k, v, do, o, lse
+        del dev, q, k, v, do, res
         torch.cuda.empty_cache()
 
 
