@@ -1,8 +1,9 @@
 """Oracle A: exact softmax attention in float64 (test infrastructure only).
 
 Definition followed (page 3, "Flash Attention: from academic breakthrough to
-industry standard" -- FlashAttention computes exact attention; the north-star
-operation is softmax(scale * Q K^T) V with a logsumexp per row):
+industry standard" -- FlashAttention computes exact attention, so the
+operation is softmax(scale * Q K^T) V, with a logsumexp per row for the
+backward):
 
   S_ij  = scale * sum_t q_it k_jt        (S_ij = -inf for j > i when causal)
   r_i   = max_j S_ij
