@@ -122,6 +122,8 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     stab = True
 
+    # one step = fa_fwd, then fa_bwd's two launches (row-dot, then dQ/dK/dV
+    # in one launch), with events between the launches
     def step(ev=None):
         if ev is not None:
             ev[0].record()
@@ -131,17 +133,14 @@ def main():
         fa.bwd_dot(o, do, dvec)
         if ev is not None:
             ev[2].record()
-        fa.bwd_dkdv(q, k, v, do, lse, dvec, causal=True, dk=dk, dv=dv)
+        fa.bwd_grads(q, k, v, do, lse, dvec, causal=True, dq=dq, dk=dk, dv=dv)
         if ev is not None:
             ev[3].record()
-        fa.bwd_dq(q, k, v, do, lse, dvec, causal=True, dq=dq)
-        if ev is not None:
-            ev[4].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
@@ -149,7 +148,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_step = wall * 1e3 / args.steps
-    names = ["fwd", "bwd_dot", "bwd_dkdv", "bwd_dq"]
+    names = ["fwd", "bwd_dot", "bwd_grads"]
     kern_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events])) for i, n in enumerate(names)}
 
     # stabilise off: forward only, for the cost of the fix
@@ -170,14 +169,13 @@ def main():
     bwd_flop = 2.5 * fwd_flop
     step_flop = fwd_flop + bwd_flop
     value = step_flop / (ms_step * 1e-3) / 1e12
-    # algorithmic FLOP attributed to each kernel: the dK/dV kernel carries four of
-    # the backward's five products (S, dP, dV, dK), the dQ kernel the fifth.
-    kflop = {"fwd": fwd_flop, "bwd_dot": 0.0, "bwd_dkdv": 0.8 * bwd_flop, "bwd_dq": 0.2 * bwd_flop}
+    # algorithmic FLOP attributed to each kernel: the dQ/dK/dV launch carries
+    # the backward's five products (its recomputed S and dP are not counted)
+    kflop = {"fwd": fwd_flop, "bwd_dot": 0.0, "bwd_grads": bwd_flop}
     elem = B * H * N * d
     kbytes = {"fwd": 4 * elem * 2 + B * H * N * 4, "bwd_dot": 2 * elem * 2 + B * H * N * 4,
-              "bwd_dkdv": 6 * elem * 2 + 2 * B * H * N * 4, "bwd_dq": 5 * elem * 2 + 2 * B * H * N * 4}
-    kernel_names = {"fwd": "fwd_kernel", "bwd_dot": "bwd_dot_kernel", "bwd_dkdv": "bwd_dkdv_kernel",
-                    "bwd_dq": "bwd_dq_kernel"}
+              "bwd_grads": 7 * elem * 2 + 2 * B * H * N * 4}
+    kernel_names = {"fwd": "fwd_kernel", "bwd_dot": "bwd_dot_kernel", "bwd_grads": "bwd_grads_kernel"}
     kernels = {}
     for n in names:
         t = kern_ms[n] * 1e-3

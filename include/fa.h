@@ -93,19 +93,22 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int causal);
  *        LSE              fp32 (B,H,N) from fa_fwd
  *        workspace        device memory of at least fa_bwd_workspace_bytes()
  *   out: dQ, dK, dV       bf16 (B,H,N,d)
- * Runs fa_bwd_dot, fa_bwd_dkdv and fa_bwd_dq in that order on `stream`
- * (three launches).  Deterministic: no atomics. */
+ * Runs fa_bwd_dot, then fa_bwd_grads, on `stream` (two launches).
+ * Deterministic: no atomics. */
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
            const float* LSE, void* dQ, void* dK, void* dV,
            void* workspace, size_t workspace_bytes,
            int B, int H, int N, int d, int causal, float scale, int stabilize,
            void* stream);
 
-/* The three steps of fa_bwd, exposed so that each can be timed on its own.
- *   fa_bwd_dot : Dvec[b,h,i] = sum_t dO[b,h,i,t] * O[b,h,i,t]   (fp32 out)
- *   fa_bwd_dkdv: dK, dV for every key, from Q, K, V, dO, LSE, Dvec
- *   fa_bwd_dq  : dQ for every query, from Q, K, V, dO, LSE, Dvec
- * Dvec is fp32 (B,H,N) device memory owned by the caller. */
+/* The steps of fa_bwd, exposed so that each can be timed on its own.
+ *   fa_bwd_dot  : Dvec[b,h,i] = sum_t dO[b,h,i,t] * O[b,h,i,t]   (fp32 out)
+ *   fa_bwd_dkdv : dK, dV for every key, from Q, K, V, dO, LSE, Dvec
+ *   fa_bwd_dq   : dQ for every query, from Q, K, V, dO, LSE, Dvec
+ *   fa_bwd_grads: dQ, dK and dV in one launch: the workgroups of the two
+ *                 kernels above, interleaved per head (what fa_bwd runs)
+ * Dvec is fp32 (B,H,N) device memory owned by the caller.  The results of
+ * fa_bwd_grads are bitwise those of fa_bwd_dkdv and fa_bwd_dq. */
 int fa_bwd_dot(const void* O, const void* dO, float* Dvec,
                int B, int H, int N, int d, void* stream);
 int fa_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO,
@@ -114,6 +117,9 @@ int fa_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO,
 int fa_bwd_dq(const void* Q, const void* K, const void* V, const void* dO,
               const float* LSE, const float* Dvec, void* dQ,
               int B, int H, int N, int d, int causal, float scale, void* stream);
+int fa_bwd_grads(const void* Q, const void* K, const void* V, const void* dO,
+                 const float* LSE, const float* Dvec, void* dQ, void* dK, void* dV,
+                 int B, int H, int N, int d, int causal, float scale, void* stream);
 
 /* Element type of the 16-bit tensors. */
 typedef enum {

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     FAError,
     bwd,
     bwd_ex,
+    bwd_grads,
     bwd_dkdv,
     bwd_dot,
     bwd_dq,

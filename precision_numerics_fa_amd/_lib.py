@@ -23,6 +23,7 @@ _SIGNATURES = {
     "fa_bwd_dot": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "fa_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
+    "fa_bwd_grads": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "fa_fwd_ex": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_ex": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
@@ -218,6 +219,23 @@ def bwd_dkdv(q, k, v, do, lse, dvec, causal: bool = False, scale: Optional[float
     _call("fa_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dvec), _ptr(dk), _ptr(dv),
           B, H, N, d, int(bool(causal)), _scale(scale, d), _stream())
     return dk, dv
+
+
+def bwd_grads(q, k, v, do, lse, dvec, causal: bool = False, scale: Optional[float] = None,
+              dq=None, dk=None, dv=None):
+    """dQ, dK, dV in one launch (what bwd runs after bwd_dot)."""
+    torch = _torch()
+    B, H, N, d = _shape(q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for n, t in (("q", q), ("k", k), ("v", v), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(n, t, torch.bfloat16, (B, H, N, d), q.device)
+    _check("lse", lse, torch.float32, (B, H, N), q.device)
+    _check("dvec", dvec, torch.float32, (B, H, N), q.device)
+    _call("fa_bwd_grads", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dvec), _ptr(dq), _ptr(dk),
+          _ptr(dv), B, H, N, d, int(bool(causal)), _scale(scale, d), _stream())
+    return dq, dk, dv
 
 
 def bwd_dq(q, k, v, do, lse, dvec, causal: bool = False, scale: Optional[float] = None, dq=None):

@@ -93,8 +93,7 @@ int bwd_impl(int dtype, const void* Q, const void* K, const void* V, const void*
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if ((st = launched(fa::launch_bwd_dot(a, s))) != FA_OK) return st;
-  if ((st = launched(fa::launch_bwd_dkdv(a, s))) != FA_OK) return st;
-  return launched(fa::launch_bwd_dq(a, s));
+  return launched(fa::launch_bwd_grads(a, s));
 }
 
 }  // namespace
@@ -157,6 +156,17 @@ int fa_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const
   fa::BwdArgs a{Q, K, V, nullptr, dO, LSE, const_cast<float*>(Dvec), dQ, nullptr, nullptr, B, H, N, d, causal != 0, scale};
   (void)hipGetLastError();
   return launched(fa::launch_bwd_dq(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd_grads(const void* Q, const void* K, const void* V, const void* dO, const float* LSE, const float* Dvec,
+                 void* dQ, void* dK, void* dV, int B, int H, int N, int d, int causal, float scale, void* stream) {
+  int st = bwd_args(Q, K, V, dO, LSE, Dvec, B, H, N, d, scale);
+  if (st != FA_OK) return st;
+  if (!aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16)) return FA_ERR_INVALID_ARG;
+  if ((st = check_device()) != FA_OK) return st;
+  fa::BwdArgs a{Q, K, V, nullptr, dO, LSE, const_cast<float*>(Dvec), dQ, dK, dV, B, H, N, d, causal != 0, scale};
+  (void)hipGetLastError();
+  return launched(fa::launch_bwd_grads(a, static_cast<hipStream_t>(stream)));
 }
 
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,

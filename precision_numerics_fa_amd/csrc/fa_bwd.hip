@@ -141,6 +141,9 @@ struct DkdvTile {
   static constexpr int NT = 256;
   static constexpr int PER = BS * D / 8 / NT;  // 16-byte copies per lane per tile
   static constexpr int KPER = B32 * D / 8 / NT;
+  static constexpr int KTILE_BYTES = B32 * D * 2;
+  static constexpr int STAGE_BYTES = 2 * 2 * TILE * 2;     // two stages of (Q, dO)
+  static constexpr int LDS_BYTES = KTILE_BYTES + STAGE_BYTES + 2 * 2 * BS * 4;
 };
 
 // ---------------------------------------------------------------- dK, dV
@@ -151,21 +154,16 @@ struct DkdvTile {
 // dO^T and Q^T come from the swizzled tiles through the transposing LDS read.
 // The register footprint allows two waves per SIMD.
 template <typename E, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
-    bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int N, int n_kblk, int total_blocks,
-    int xcd_remap, float c2, float scale) {
+__device__ __forceinline__ void dkdv_wg(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
+                                        const bf16_t* __restrict__ V, const bf16_t* __restrict__ dO,
+                                        const float* __restrict__ LSE, const float* __restrict__ Dvec,
+                                        bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int N, float c2,
+                                        float scale, int bh, int kb, unsigned char* lds) {
   using T = DkdvTile<D>;
-  __shared__ __attribute__((aligned(16))) bf16_t ktile[T::B32 * D];
-  // two stages of (Q tile, dO tile) and of (LSE, D) for the block's rows
-  __shared__ __attribute__((aligned(16))) bf16_t tiles[2][2 * T::TILE];
-  __shared__ __attribute__((aligned(16))) float vecs[2][2 * T::BS];
-
-  int bid = blockIdx.x;
-  if (xcd_remap) bid = (bid & 7) * (total_blocks >> 3) + (bid >> 3);
-  const int bh = bid / n_kblk;
-  const int kb = bid - bh * n_kblk;  // causal: the first key blocks carry the most work
+  // LDS: the K tile, two stages of (Q tile, dO tile), two of (LSE, D)
+  bf16_t* const ktile = reinterpret_cast<bf16_t*>(lds);
+  bf16_t(*const tiles)[2 * T::TILE] = reinterpret_cast<bf16_t(*)[2 * T::TILE]>(lds + T::KTILE_BYTES);
+  float(*const vecs)[2 * T::BS] = reinterpret_cast<float(*)[2 * T::BS]>(lds + T::KTILE_BYTES + T::STAGE_BYTES);
   const int k0 = kb * T::B32;
 
   const int tid = threadIdx.x;
@@ -325,23 +323,19 @@ struct DqTile {
   static constexpr int TILE = BS * D;      // one swizzled tile (elements)
   static constexpr int NT = 256;
   static constexpr int PER = BS * D / 8 / NT;  // 16-byte loads per lane per tile
+  static constexpr int LDS_BYTES = 4 * TILE * 2;
 };
 
 // ---------------------------------------------------------------- dQ
 template <typename E, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
-    bf16_t* __restrict__ dQ, int N, int n_qblk, int total_blocks, int xcd_remap, float c2,
-    float scale) {
+__device__ __forceinline__ void dq_wg(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
+                                      const bf16_t* __restrict__ V, const bf16_t* __restrict__ dO,
+                                      const float* __restrict__ LSE, const float* __restrict__ Dvec,
+                                      bf16_t* __restrict__ dQ, int N, float c2, float scale, int bh, int qb,
+                                      unsigned char* lds) {
   using T = DqTile<D>;
-  // ring of two (K tile, V tile) pairs
-  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * T::TILE];
-
-  int bid = blockIdx.x;
-  if (xcd_remap) bid = (bid & 7) * (total_blocks >> 3) + (bid >> 3);
-  const int bh = bid / n_qblk;
-  const int qb = n_qblk - 1 - (bid - bh * n_qblk);
+  // LDS: a ring of two (K tile, V tile) pairs
+  bf16_t* const smem = reinterpret_cast<bf16_t*>(lds);
   const int q0 = qb * T::B32;
 
   const int tid = threadIdx.x;
@@ -459,6 +453,73 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   if (wave_live && myq < N) store_row<E, D>(dQ + hoff + (size_t)myq * D, dq, scale, hi);
 }
 
+// Workgroup index -> work item: the hardware hands workgroup i to XCD i % 8;
+// the remap gives each XCD a contiguous range of the logical order (heads
+// stay within one XCD's L2).
+__device__ __forceinline__ int logical_block(int total_blocks, int xcd_remap) {
+  const int bid = blockIdx.x;
+  return xcd_remap ? (bid & 7) * (total_blocks >> 3) + (bid >> 3) : bid;
+}
+
+// dK, dV of one 128-key block per workgroup; causal: the first key blocks
+// (the most work) first.
+template <typename E, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
+    bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int N, int n_kblk, int total_blocks,
+    int xcd_remap, float c2, float scale) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[DkdvTile<D>::LDS_BYTES];
+  const int bid = logical_block(total_blocks, xcd_remap);
+  const int bh = bid / n_kblk;
+  dkdv_wg<E, D, CAUSAL>(Q, K, V, dO, LSE, Dvec, dK, dV, N, c2, scale, bh, bid - bh * n_kblk, lds);
+}
+
+// dQ of one 128-query block per workgroup; causal: the last query blocks
+// (the most work) first.
+template <typename E, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
+    bf16_t* __restrict__ dQ, int N, int n_qblk, int total_blocks, int xcd_remap, float c2,
+    float scale) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[DqTile<D>::LDS_BYTES];
+  const int bid = logical_block(total_blocks, xcd_remap);
+  const int bh = bid / n_qblk;
+  dq_wg<E, D, CAUSAL>(Q, K, V, dO, LSE, Dvec, dQ, N, c2, scale, bh, n_qblk - 1 - (bid - bh * n_qblk), lds);
+}
+
+// dK/dV and dQ in one launch.  The heads are split into (at most) eight
+// groups of G, one per XCD; in each group the dK/dV workgroups (128 keys)
+// come first and then the dQ workgroups (128 queries), each kind heaviest
+// first, so the dQ work fills the tail of the dK/dV work on the same XCD and
+// both read the group's tensors through that XCD's L2.  The two bodies share
+// one LDS allocation (a workgroup runs one of them).  Workgroups past the
+// last head (when B*H is not a multiple of G) return at once.
+template <typename E, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_grads_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
+    bf16_t* __restrict__ dQ, bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int N, int n_blk,
+    int total_blocks, int xcd_remap, float c2, float scale, int BH, int G) {
+  constexpr int B0 = DkdvTile<D>::LDS_BYTES, B1 = DqTile<D>::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[B0 > B1 ? B0 : B1];
+  const int bid = logical_block(total_blocks, xcd_remap);
+  // heads in groups of G (one group per XCD): a group's dK/dV workgroups
+  // first, then its dQ workgroups
+  const int per_group = 2 * G * n_blk;
+  const int g = bid / per_group;
+  const int r = bid - g * per_group;
+  const bool is_dq = r >= G * n_blk;
+  const int r2 = is_dq ? r - G * n_blk : r;
+  const int bh = g * G + r2 / n_blk;
+  if (bh >= BH) return;
+  if (is_dq)
+    dq_wg<E, D, CAUSAL>(Q, K, V, dO, LSE, Dvec, dQ, N, c2, scale, bh, n_blk - 1 - r2 % n_blk, lds);
+  else
+    dkdv_wg<E, D, CAUSAL>(Q, K, V, dO, LSE, Dvec, dK, dV, N, c2, scale, bh, r2 % n_blk, lds);
+}
+
 inline int remap_ok(long long total) { return (total % 8 == 0) ? 1 : 0; }
 
 template <typename E, int D>
@@ -493,6 +554,26 @@ hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename E, int D, bool CAUSAL>
+hipError_t launch_grads_t(const BwdArgs& a, hipStream_t s) {
+  static_assert(DkdvTile<D>::B32 == DqTile<D>::B32, "one block count for both kinds");
+  const int n_blk = (a.N + DkdvTile<D>::B32 - 1) / DkdvTile<D>::B32;
+  const int BH = a.B * a.H;
+  const int G = (BH + 7) / 8;  // heads per group: one group per XCD
+  const long long total = (long long)((BH + G - 1) / G) * 2 * G * n_blk;
+  hipLaunchKernelGGL((bwd_grads_kernel<E, D, CAUSAL>), dim3((unsigned)total), dim3(256), 0, s,
+                     (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.dout,
+                     a.lse, a.dvec, (bf16_t*)a.dq, (bf16_t*)a.dk, (bf16_t*)a.dv, a.N, n_blk, (int)total,
+                     remap_ok(total), scale_log2e(a.scale), a.scale, BH, G);
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t grads_e(const BwdArgs& a, hipStream_t s) {
+  if (a.d == 64) return a.causal ? launch_grads_t<E, 64, true>(a, s) : launch_grads_t<E, 64, false>(a, s);
+  return a.causal ? launch_grads_t<E, 128, true>(a, s) : launch_grads_t<E, 128, false>(a, s);
+}
+
 template <typename E>
 hipError_t dot_e(const BwdArgs& a, hipStream_t s) {
   return a.d == 64 ? launch_dot_t<E, 64>(a, s) : launch_dot_t<E, 128>(a, s);
@@ -522,6 +603,10 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s) {
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s) {
   return a.dtype == kF16 ? dq_e<_Float16>(a, s) : dq_e<__bf16>(a, s);
+}
+
+hipError_t launch_bwd_grads(const BwdArgs& a, hipStream_t s) {
+  return a.dtype == kF16 ? grads_e<_Float16>(a, s) : grads_e<__bf16>(a, s);
 }
 
 }  // namespace fa

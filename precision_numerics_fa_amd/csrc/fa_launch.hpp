@@ -47,6 +47,8 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dot(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
+// dK, dV and dQ in one launch (the two kernels above, fused horizontally)
+hipError_t launch_bwd_grads(const BwdArgs& a, hipStream_t stream);
 
 // scale * log2(e), rounded once to fp32 (the factor that folds the softmax
 // scale into the base-2 exponent).

@@ -87,6 +87,8 @@ def test_backward_argument_validation(lib):
     assert lib.fa_bwd_dot(GOOD, None, GOOD, 1, 1, 8, 64, None) == -1
     assert lib.fa_bwd_dkdv(*[GOOD] * 6, P(4097), GOOD, 1, 1, 8, 64, 1, 0.125, None) == -1
     assert lib.fa_bwd_dq(*[GOOD] * 6, GOOD, 1, 1, 8, 64, 1, -1.0, None) == -1
+    assert lib.fa_bwd_grads(*[GOOD] * 6, GOOD, P(4100), GOOD, 1, 1, 8, 64, 1, 0.125, None) == -1
+    assert lib.fa_bwd_grads(*[GOOD] * 9, 1, 1, 8, 80, 1, 0.125, None) == -2
 
 
 def test_typed_entry_points_validate_dtype_and_arguments(lib):

@@ -142,6 +142,27 @@ def test_constant_value_column_is_reproduced(fa):
             assert np.abs(of[..., 77] + 0.625).max() <= 0.625 * 2 ** -7
 
 
+@pytest.mark.parametrize("B,H,N,d,causal", [(1, 3, 200, 64, True), (2, 5, 333, 128, True),
+                                             (1, 2, 130, 128, False), (4, 8, 1024, 64, True),
+                                             (1, 1, 1, 64, False)])
+def test_fused_grads_equal_the_separate_kernels(fa, B, H, N, d, causal):
+    """fa_bwd_grads (what fa_bwd runs) interleaves the dK/dV and dQ workgroups
+    in one launch, with head groups that need not divide B*H: its results are
+    bitwise those of fa_bwd_dkdv and fa_bwd_dq."""
+    import torch
+    say(f"fused grads B={B} H={H} N={N} d={d} causal={causal}")
+    bits, dev = random_case(B, H, N, d, seed=N + 5 * d + H, with_do=True)
+    o, lse = fa.fwd(dev["q"], dev["k"], dev["v"], causal=causal, stabilize=True)
+    dvec = fa.bwd_dot(o, dev["do"])
+    args = (dev["q"], dev["k"], dev["v"], dev["do"], lse, dvec)
+    dk1, dv1 = fa.bwd_dkdv(*args, causal=causal)
+    dq1 = fa.bwd_dq(*args, causal=causal)
+    dq2, dk2, dv2 = fa.bwd_grads(*args, causal=causal)
+    dq3, dk3, dv3 = fa.bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=causal)
+    for a, b, c in ((dq1, dq2, dq3), (dk1, dk2, dk3), (dv1, dv2, dv3)):
+        assert torch.equal(a, b) and torch.equal(a, c)
+
+
 def test_forward_and_backward_are_deterministic(fa):
     import torch
     say("invariant: determinism")
