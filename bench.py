@@ -19,6 +19,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -60,10 +61,15 @@ def copy_probe(mib: int) -> None:
 
 
 def source_digest() -> str:
+    """Digest of the kernel sources with comments and blank space removed, so
+    that the stored counter figures stay valid across comment-only edits."""
     h = hashlib.sha256()
     for s in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "precision_numerics_fa_amd", "csrc", s), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "precision_numerics_fa_amd", "csrc", s)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

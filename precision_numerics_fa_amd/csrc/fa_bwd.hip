@@ -13,23 +13,25 @@
 // Page 1 (section 4.3) notes that gradients of Q and K inherit the forward's
 // errors through these quantities; the recipe itself is the standard one.
 //
-// Two compute kernels, no atomics, deterministic:
-//   bwd_dkdv: a workgroup owns 128 keys (32 per wave; K rows in an LDS tile,
+// Two kinds of compute workgroup, no atomics, deterministic:
+//   dK/dV: a workgroup owns 128 keys (32 per wave; K rows in an LDS tile,
 //     V rows in registers as B operands) and walks 32-query blocks of Q and
 //     dO.  It works in the S layout (rows = queries, lane = key), so P and dS
 //     are already B operands of dV^T = dO^T P and dK^T = Q^T dS, whose A
 //     operands dO^T and Q^T come from the LDS tiles through the transposing
 //     LDS read.
-//   bwd_dq: a workgroup owns 128 queries (Q and dO rows in registers) and
+//   dQ: a workgroup owns 128 queries (Q and dO rows in registers) and
 //     walks 64-key blocks of K and V in LDS.  It works in the S^T layout
 //     (lane = query), so dS^T is the B operand of dQ^T = K^T dS^T, whose A
 //     operand K^T is a transposing read of the K tile.
 // Scores and dP are recomputed in both (7 products instead of 5), which buys
 // determinism and no LDS round trip of P or dS.  All tiles are swizzled and
-// copied straight from HBM into LDS, one block ahead.  Both kernels keep
+// copied straight from HBM into LDS, one block ahead.  Both kinds keep
 // their register footprint within two waves per SIMD: the MFMAs of one wave
 // then overlap the exponential and elementwise work of the other, which the
 // hardware arbitrates better than a single wave's own instruction order.
+// bwd_grads_kernel runs both kinds in one launch (what fa_bwd uses);
+// bwd_dkdv_kernel and bwd_dq_kernel run one kind each.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
