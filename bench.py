@@ -73,10 +73,10 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic(kernel: str):
-    """HBM bytes per launch for `kernel` from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+def _counter_record(name: str, kernel: str):
+    """Per-kernel record of a committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", name)
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -84,8 +84,20 @@ def counter_traffic(kernel: str):
         return None
     if rec.get("source_digest") != source_digest():
         return None
-    k = rec.get("kernels", {}).get(kernel)
+    return rec.get("kernels", {}).get(kernel)
+
+
+def counter_traffic(kernel: str):
+    """HBM bytes per launch for `kernel` (FETCH_SIZE + WRITE_SIZE, calibrated)."""
+    k = _counter_record("hbm_traffic.json", kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def counter_mfma_busy(kernel: str):
+    """Fraction of the kernel's cycles the MFMA pipes were busy (SQ counters,
+    every MFMA counted, recomputation included; independent of the clock)."""
+    k = _counter_record("sq_counters.json", kernel)
+    return None if k is None else k.get("mfma_pipe_busy")
 
 
 def main():
@@ -194,6 +206,8 @@ def main():
             kernels[n] = {"ms": round(kern_ms[n], 4), "bound": "hbm", "achieved": round(ach, 1),
                           "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
         kernels[n]["traffic"] = counter_traffic(kernel_names[n])
+        if kflop[n] > 0:
+            kernels[n]["mfma_pipe_busy"] = counter_mfma_busy(kernel_names[n])
     dominant = max(names, key=lambda n: kern_ms[n])
     roofline = dict(kernels[dominant])
     roofline.pop("ms")
