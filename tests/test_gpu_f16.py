@@ -92,6 +92,36 @@ def test_f16_bwd_small_against_oracle(fa, B, H, N, d, causal):
         assert rel <= GRAD_REL, (name, rel)
 
 
+@pytest.mark.parametrize("mult", [1.0, 8.0])
+def test_f16_identical_keys_give_mean_of_values(fa, mult):
+    """Every row's maximum repeats N times; with Q, K x 8, |R| is in the
+    hundreds and the binary16 fold puts the shared probability in [1/2, 1).
+    Each probability is the same binary16 value (11 significant bits), so O
+    is the mean of V to half an output ulp, 2^-11 relative, and the fp32
+    summation error."""
+    say(f"f16 invariant: identical keys, mult={mult}")
+    for d in (64, 128):
+        B, H, N = 1, 2, 192
+        bits, dev = random_case(B, H, N, d, seed=12, mult=mult, dtype="f16")
+        k = dev["k"][:, :, :1].expand(B, H, N, d).contiguous()
+        v = head_f64(bits["v"], "f16")
+        for causal in (False, True):
+            if causal:
+                cnt = np.arange(1, N + 1)[None, None, :, None]
+                mean = np.cumsum(v, axis=2) / cnt
+                mabs = np.cumsum(np.abs(v), axis=2) / cnt
+            else:
+                mean = np.broadcast_to(v.mean(axis=2, keepdims=True), v.shape)
+                mabs = np.broadcast_to(np.abs(v).mean(axis=2, keepdims=True), v.shape)
+            for stab in (False, True):
+                o, _ = fa.fwd_ex(dev["q"], k, dev["v"], causal=causal, stabilize=stab)
+                # output rounding, the shared probability's rounding, and the
+                # fp32 sums (at most N * 2^-24 of the mean of |v|)
+                bound = (0.5 * Mt.f16_ulp(mean) + np.abs(mean) * (2.0 ** -11 if stab else 0.0)
+                         + N * 2.0 ** -24 * mabs)
+                assert (np.abs(to_f64(o) - mean) <= bound).all(), (d, causal, stab)
+
+
 def test_f16_close_to_emulation(fa):
     """Against the binary16 emulation: most outputs agree to the bit.  The rest
     differ where the GPU's exp2 or summation order flips the binary16 rounding
