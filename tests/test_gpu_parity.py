@@ -320,3 +320,42 @@ def test_gpu_close_to_emulation(fa):
         ulps = np.abs(of - ob) / Mt.bf16_ulp(ob)
         say(f"  emulation agreement stabilize={stab}: identical {same:.3f}, max ulps {ulps.max():.1f}")
         assert same > 0.5 and ulps.max() <= 4
+
+
+def test_graph_capture_replays_match_eager(fa):
+    """fa_fwd and fa_bwd enqueue kernels only (no allocation, copy or memset
+    inside the library), so a HIP graph can capture them.  The graph is
+    replayed three times, with eager work and synchronisation between the
+    replays, and every replay must equal the eager result bitwise."""
+    import torch
+    say("graph capture: forward + backward")
+    w = F.WORKLOADS["c5"].with_shape(B=2, H=4, N=512)
+    full, dev = device_inputs(w)
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    o_e, l_e = fa.fwd(q, k, v, causal=True, stabilize=True)
+    g_e = fa.bwd(q, k, v, o_e, do, l_e, causal=True)
+    torch.cuda.synchronize()
+    o = torch.empty_like(q)
+    lse = torch.empty_like(l_e)
+    ws = torch.empty(fa.workspace_bytes(w.B, w.H, w.N, w.d, True), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up on the capture stream
+        fa.fwd(q, k, v, causal=True, stabilize=True, out=o, lse=lse)
+        grads = fa.bwd(q, k, v, o, do, lse, causal=True, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fa.fwd(q, k, v, causal=True, stabilize=True, out=o, lse=lse)
+        grads = fa.bwd(q, k, v, o, do, lse, causal=True, workspace=ws)
+    for rep in range(3):
+        for t in (o, lse, *grads):
+            t.zero_()
+        fa.fwd(q, k, v, causal=False, stabilize=False)  # unrelated eager work
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_e) and torch.equal(lse, l_e), rep
+        for a, b in zip(grads, g_e):
+            assert torch.equal(a, b), rep
