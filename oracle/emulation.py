@@ -40,6 +40,12 @@ its constants are parameters:
     same power-of-two maximum 2^-64, whose bf16 rounding is exact: the fix
     would do nothing for them.)
 
+For binary16 (``fmt="f16"``) the same rule folds |R| by whole units into
+(0, 1] (``RULES["f16"]``): binary16's normal numbers end at 2^-14, so the
+bf16 constants would let the largest probability 2^-|R| underflow once
+|R| > 24.  A whole-unit fold rescales by a power of two only, so the rounding
+of the largest probability stays that of 2^-|R|.
+
 The size of the bias this rule removes, and the constants, are parity
 unpinned: the pages give no number for them.
 
