@@ -154,7 +154,8 @@ def test_constant_value_column_is_reproduced(fa):
 
 @pytest.mark.parametrize("B,H,N,d,causal", [(1, 3, 200, 64, True), (2, 5, 333, 128, True),
                                              (1, 2, 130, 128, False), (4, 8, 1024, 64, True),
-                                             (1, 1, 1, 64, False)])
+                                             (1, 1, 1, 64, False), (3, 3, 100, 64, True),
+                                             (1, 17, 70, 128, False)])
 def test_fused_grads_equal_the_separate_kernels(fa, B, H, N, d, causal):
     """fa_bwd_grads (what fa_bwd runs) interleaves the dK/dV and dQ workgroups
     in one launch, with head groups that need not divide B*H: its results are
