@@ -1,4 +1,6 @@
-// Tiled BF16 attention forward for gfx950 (MI355X).
+// Tiled BF16 attention forward for gfx950 (MI355X); the same kernel serves
+// IEEE binary16 tensors (the element type E is a template parameter: it
+// selects the MFMA and the 16-bit rounding, everything else is shared).
 //
 // The method (page 3, "Flash Attention: from academic breakthrough to
 // industry standard"; page 2, "Mechanism 2: where the bias comes from"):
@@ -24,6 +26,9 @@
 // LDS read.  O^T and l stay in registers until the epilogue.  The scores of
 // block j+1 are issued in the same basic block as the softmax of block j, so
 // the MFMAs of one overlap the VALU/exponential work of the other.
+//
+// Workgroups map to (head, query block) in per-XCD head groups, head-major
+// or, for small launches, block-major (see the kernel's first lines).
 //
 // Exponentials use exp2 with scale*log2(e) folded into one FMA:
 // P = 2^(t*c - M), t the raw FP32 dot product, c = scale*log2 e, M the shift
