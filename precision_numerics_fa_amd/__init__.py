@@ -8,6 +8,7 @@ not a gfx950 GPU, the calls raise.
 
     o, lse = fwd(q, k, v, causal=True, stabilize=True)
     dq, dk, dv = bwd(q, k, v, o, do, lse, causal=True)
+    o = attention(q, k, v, causal=True, stabilize=True)   # differentiable (autograd)
 
 Tensors are torch.bfloat16, shape (B, H, N, d), contiguous, on the current
 CUDA (HIP) device; LSE is float32 (B, H, N).  fwd_ex / bwd_ex take
@@ -17,6 +18,7 @@ from ._lib import (  # noqa: F401
     FA_BF16,
     FA_F16,
     FAError,
+    attention,
     bwd,
     bwd_ex,
     bwd_grads,

@@ -300,3 +300,40 @@ def bwd_ex(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = N
           _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, N, d,
           int(bool(causal)), _scale(scale, d), int(bool(stabilize)), _stream())
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------- autograd
+
+def attention(q, k, v, causal: bool = False, scale: Optional[float] = None, stabilize: bool = False):
+    """softmax(scale * q k^T) v as a differentiable torch op: the forward is
+    fa_fwd_ex and the backward fa_bwd_ex (bfloat16 or float16 tensors,
+    (B, H, N, d), contiguous).  Only the marshalling is Python."""
+    return _attention_fn().apply(q, k, v, bool(causal), scale, bool(stabilize))
+
+
+_ATTN = None
+
+
+def _attention_fn():
+    global _ATTN
+    if _ATTN is None:
+        torch = _torch()
+
+        class _Attention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, causal, scale, stabilize):
+                q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+                o, lse = fwd_ex(q, k, v, causal=causal, scale=scale, stabilize=stabilize)
+                ctx.save_for_backward(q, k, v, o, lse)
+                ctx.causal, ctx.scale, ctx.stabilize = causal, scale, stabilize
+                return o
+
+            @staticmethod
+            def backward(ctx, do):
+                q, k, v, o, lse = ctx.saved_tensors
+                dq, dk, dv = bwd_ex(q, k, v, o, do.contiguous(), lse, causal=ctx.causal, scale=ctx.scale,
+                                    stabilize=ctx.stabilize)
+                return dq, dk, dv, None, None, None
+
+        _ATTN = _Attention
+    return _ATTN

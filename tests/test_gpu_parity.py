@@ -360,3 +360,21 @@ def test_graph_capture_replays_match_eager(fa):
         assert torch.equal(o, o_e) and torch.equal(lse, l_e), rep
         for a, b in zip(grads, g_e):
             assert torch.equal(a, b), rep
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_autograd_attention_matches_the_abi_calls(fa, dtype):
+    """attention() is a torch.autograd.Function over fa_fwd_ex / fa_bwd_ex:
+    its output and the gradients autograd returns are bitwise the direct
+    calls'."""
+    import torch
+    say(f"autograd attention {dtype}")
+    bits, dev = random_case(2, 3, 150, 64, seed=77, with_do=True, dtype=dtype)
+    q, k, v = (dev[n].clone().requires_grad_(True) for n in ("q", "k", "v"))
+    o = fa.attention(q, k, v, causal=True, stabilize=True)
+    o.backward(dev["do"])
+    o2, lse = fa.fwd_ex(dev["q"], dev["k"], dev["v"], causal=True, stabilize=True)
+    g2 = fa.bwd_ex(dev["q"], dev["k"], dev["v"], o2, dev["do"], lse, causal=True)
+    assert torch.equal(o.detach(), o2)
+    for t, g in zip((q, k, v), g2):
+        assert torch.equal(t.grad, g)
