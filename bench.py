@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step benchmark, time the forward (fix on and off) and the "
                          "backward on every workload c1..c5 and print one JSON line per workload")
+    ap.add_argument("--bias-toy", action="store_true",
+                    help="instead of the step benchmark, measure how the attention gradient's "
+                         "rounding error accumulates over training steps of a toy attention layer "
+                         "with repeated tokens, fix off and on (one JSON line)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB a few times "
                          "(calibrates the HBM byte counters) and exit")
@@ -124,6 +128,9 @@ def main():
     fa.load()
     if args.sweep:
         sweep(args)
+        return
+    if args.bias_toy:
+        bias_toy(args)
         return
 
     w = F.WORKLOADS["c4"].with_shape(with_do=True)
@@ -388,6 +395,128 @@ def cpu_baseline_leg(w, full, o, lse, dq, dk, dv, heads, step_flop):
                      "dq_rel": errs["dq"], "dk_rel": errs["dk"], "dv_rel": errs["dv"]},
     }
 
+
+def bias_toy(args, T: int = 300, gain: float = 12.0):
+    """Bias accumulation in a toy attention layer (page 2, "Mechanism 1" and
+    "Mechanism 2": a rounding error that is not zero-mean, met again and again
+    along similar low-rank update directions, adds up in the weights instead of
+    averaging out).
+
+    One head, d = 64, B = 8 sequences of N = 256 tokens, a fresh batch every
+    step.  Token inputs are low-rank (rank 4 plus a shared component and 10%
+    noise).  Queries and values read the token input; keys read a key input
+    that equals it except at two "sink" positions per sequence, which carry one
+    fixed large vector: their keys are identical, their values are not, and
+    where they hold most of a row's attention they tie at its maximum.
+    q = x W_Q, k = a W_K, v = x W_V; the loss is the mean squared distance of
+    the output to a fixed linear map of x.  The control run gives the second
+    sink a slightly different key input: no ties, the same attention mass.
+
+    Along the float32 reference trajectory (plain SGD on reference gradients),
+    the W_Q, W_K, W_V gradients through fa_fwd/fa_bwd (fix off, fix on) are
+    compared at every step with the float32 ones on the same bf16 Q, K, V.
+    With per-step errors e_t, |sum e_t| / sqrt(sum |e_t|^2) is about 1 for
+    independent errors and sqrt(T) for errors that keep one direction.  Each
+    variant also trains on its own gradients; the spectral norms of W_Q and
+    W_K after T steps, and the distance from the reference weights, follow.
+    """
+    import numpy as np
+    import torch
+
+    import precision_numerics_fa_amd as fa
+
+    B, N, dm, r = 8, 256, 64, 4
+    rng = np.random.default_rng([2024, 0xB1A5])
+    cuda = lambda a: torch.from_numpy(a.astype(np.float32)).cuda()  # noqa: E731
+    basis = cuda(rng.standard_normal((r, dm)) / math.sqrt(r))
+    common = cuda(rng.standard_normal(dm))
+    W0 = [cuda(rng.standard_normal((dm, dm)) / math.sqrt(dm)) for _ in range(3)]
+    teacher = cuda(rng.standard_normal((dm, dm)) / math.sqrt(dm))
+    sink = cuda(rng.standard_normal(dm))
+    sink = sink / sink.norm() * math.sqrt(dm)
+    if float((common @ W0[0]) @ (sink @ W0[1])) < 0:   # the shared query component favours the sinks
+        sink = -sink
+    sink = gain * sink
+    sink2 = {True: sink, False: sink + 0.01 * gain * cuda(rng.standard_normal(dm))}
+    scale, lr = 1.0 / math.sqrt(dm), 0.05
+    names = ("W_Q", "W_K", "W_V")
+
+    def batch(t, tied):
+        g = torch.Generator(device="cuda").manual_seed(7919 * t + 17)
+        Z = torch.randn((B, N, r), generator=g, device="cuda")
+        X = common + Z @ basis + 0.1 * torch.randn((B, N, dm), generator=g, device="cuda")
+        A = X.clone()
+        pos = torch.argsort(torch.rand((B, N), generator=g, device="cuda"), dim=1)[:, :2]
+        rows = torch.arange(B, device="cuda")
+        A[rows, pos[:, 0]] = sink
+        A[rows, pos[:, 1]] = sink2[tied]
+        return X, A, X @ teacher
+
+    def projections(Wl, X, A):
+        return [x @ w for x, w in zip((X, A, X), Wl)]
+
+    def ref_grads(Wl, X, A, Y):
+        Wt = [w.clone().requires_grad_(True) for w in Wl]
+        # bf16 values in the forward, float32 gradients straight through the rounding
+        q, k, v = [(t.to(torch.bfloat16).float() - t).detach() + t for t in projections(Wt, X, A)]
+        s = (q @ k.transpose(-1, -2).contiguous()) * scale
+        p = torch.softmax(s, dim=-1)
+        loss = ((p @ v - Y) ** 2).mean()
+        loss.backward()
+        s, p = s.detach(), p.detach()
+        tied = float(((s == s.max(dim=-1, keepdim=True).values).sum(-1) >= 2).float().mean())
+        top2 = float(p.topk(2, dim=-1).values.sum(-1).mean())
+        return [w.grad for w in Wt], float(loss.detach()), tied, top2
+
+    def fa_grads(Wl, X, A, Y, stabilize):
+        q, k, v = [t.to(torch.bfloat16).unsqueeze(1).contiguous() for t in projections(Wl, X, A)]
+        o, lse = fa.fwd(q, k, v, causal=False, stabilize=stabilize)
+        do = ((2.0 / Y.numel()) * (o.float().squeeze(1) - Y)).to(torch.bfloat16).unsqueeze(1).contiguous()
+        dq, dk, dv = fa.bwd(q, k, v, o, do, lse, causal=False)
+        return [(x.transpose(-1, -2) @ g.float().squeeze(1)).sum(0) for x, g in zip((X, A, X), (dq, dk, dv))]
+
+    def run(tied):
+        acc = {m: {"sum": [torch.zeros(dm, dm, device="cuda") for _ in names], "sq": [0.0] * 3}
+               for m in ("off", "on")}
+        W = {m: [w.clone() for w in W0] for m in ("ref", "off", "on")}
+        losses, tie_frac, top2, gnorm = [], 0.0, 0.0, [0.0] * 3
+        for t in range(T):
+            X, A, Y = batch(t, tied)
+            g_ref, loss, tf, tm = ref_grads(W["ref"], X, A, Y)
+            losses.append(loss)
+            tie_frac, top2 = tie_frac + tf / T, top2 + tm / T
+            gnorm = [a + float(g.norm()) / T for a, g in zip(gnorm, g_ref)]
+            for m, stab in (("off", False), ("on", True)):
+                g = fa_grads(W["ref"], X, A, Y, stab)
+                for i in range(3):
+                    e = g[i] - g_ref[i]
+                    acc[m]["sum"][i] += e
+                    acc[m]["sq"][i] += float((e * e).sum())
+                W[m] = [w - lr * gi for w, gi in zip(W[m], fa_grads(W[m], X, A, Y, stab))]
+            W["ref"] = [w - lr * gi for w, gi in zip(W["ref"], g_ref)]
+        torch.cuda.synchronize()
+        res = {"tied_row_fraction": round(tie_frac, 3), "top2_attention_mass": round(top2, 3),
+               "loss_first": round(losses[0], 5), "loss_last": round(losses[-1], 5),
+               "mean_ref_grad_norm": {n: float(f"{g:.3e}") for n, g in zip(names, gnorm)}}
+        for m in ("off", "on"):
+            for i, name in enumerate(names):
+                S = acc[m]["sum"][i]
+                res[f"{name}_fix_{m}"] = {
+                    "accumulation_ratio": round(float(S.norm()) / math.sqrt(acc[m]["sq"][i]), 2),
+                    "rms_error_per_step": float(f"{math.sqrt(acc[m]['sq'][i] / T):.3e}"),
+                    "accumulated_error": float(f"{float(S.norm()):.3e}")}
+        for m in ("ref", "off", "on"):
+            for i, name in enumerate(names[:2]):
+                res[f"spectral_norm_{name}_{m}"] = round(float(torch.linalg.svdvals(W[m][i].cpu())[0]), 5)
+            if m != "ref":
+                res[f"weight_distance_from_ref_{m}"] = float(
+                    f"{math.sqrt(sum(float(((a - b) ** 2).sum()) for a, b in zip(W[m], W['ref']))):.3e}")
+        return res
+
+    out = {"steps": T, "B": B, "N": N, "d": dm, "sink_gain": gain,
+           "independent_errors_ratio": 1.0, "one_direction_ratio": round(math.sqrt(T), 2),
+           "tied": run(True), "untied_control": run(False)}
+    print(json.dumps({"bias_toy": out}), flush=True)
 
 if __name__ == "__main__":
     main()
