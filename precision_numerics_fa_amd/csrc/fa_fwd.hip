@@ -249,6 +249,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   // so the next block's scores need no register copy.
   f32x16 sa[NS], sb[NS];
   if (n_wave > 0) scores(Kbuf, sa);
+  // The first iteration copies block 2 into the tile these scores were just
+  // read from; every wave's reads of it must be complete before any wave
+  // issues that copy.
+  if (n_kblk > 2) __syncthreads();
 
   auto iteration = [&](int j, f32x16* sc, f32x16* sn) {
     // Prefetch: K[j+2] into the K tile block j used, V[j+1] into the V tile
