@@ -28,4 +28,4 @@ brute force, finite differences, library routines and invariants.  The one
 part the pages give no number for -- the size of the tie bias and the shift
 constants -- is "parity unpinned" (see ``emulation``).
 """
-from . import reference, emulation, metrics  # noqa: F401
+from . import reference, emulation, baseline, metrics  # noqa: F401
