@@ -56,7 +56,7 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1,   /* NULL pointer, bad size, misalignment, bad scale */
-  FA_ERR_UNSUPPORTED = -2,   /* head dimension other than 64 / 128 */
+  FA_ERR_UNSUPPORTED = -2,   /* head dimension other than 64 / 128; baseline N > 16384 */
   FA_ERR_WORKSPACE = -3,     /* workspace NULL or smaller than fa_bwd_workspace_bytes() */
   FA_ERR_LAUNCH = -4,        /* the HIP runtime rejected a kernel launch */
   FA_ERR_DEVICE = -5         /* no gfx950 device current, or a device query failed */
@@ -149,6 +149,62 @@ int fa_bwd_ex(int dtype, const void* Q, const void* K, const void* V, const void
               void* workspace, size_t workspace_bytes,
               int B, int H, int N, int d, int causal, float scale, int stabilize,
               void* stream);
+
+/* ------------------------------------------------------------------------
+ * Baseline attention with FP32 accumulation (page 3, "What did Meta's study
+ * find": FlashAttention's numeric deviation is measured there against a
+ * baseline attention that accumulates in FP32, in an isolated BF16 forward
+ * pass).  This is the plain unfused computation, for comparison with
+ * fa_fwd on the same device and inputs; it is bound by HBM traffic on the
+ * N x N matrices it materialises:
+ *
+ *   S   = fl32(fl32(Q K^T) * scale)        FP32, (B,H,N,ld); for causal
+ *                                           attention keys j > i are not read
+ *   r_i = max_j S_ij,  e_ij = fl32(2^(fl32(S_ij - r_i) * log2 e)),
+ *   l_i = sum_j e_ij (FP32),  P_ij = bf16(e_ij * fl32(1 / l_i))
+ *   O   = bf16(P V) (FP32 accumulation),  LSE_i = r_i + ln l_i
+ *
+ * The probabilities are normalised before their BF16 cast (in fa_fwd the
+ * unnormalised ones are cast and O is divided by l at the end).  Q, K, V, O
+ * are bf16 (B,H,N,d) with d 64 or 128, LSE fp32 (B,H,N).  N is limited to
+ * 16384 (FA_ERR_UNSUPPORTED above) and B*H*N to below 2^31.  The S and P
+ * matrices have a row stride of ld = fa_base_ld(N) elements (N rounded up
+ * to 64); for causal attention only the 64-key blocks up to the diagonal
+ * are written and read.  Other conventions as above.
+ * ------------------------------------------------------------------------ */
+
+/* Row stride (in elements) of the baseline's S and P: N rounded up to 64
+ * (0 for N < 1). */
+int fa_base_ld(int N);
+
+/* Bytes of device workspace fa_base_fwd needs: S (fp32) at offset 0, then P
+ * (bf16) at the next multiple of 256 bytes, each (B,H,N,fa_base_ld(N)).
+ * Returns 0 for invalid or unsupported sizes. */
+size_t fa_base_workspace_bytes(int B, int H, int N, int d, int causal);
+
+/* The baseline forward: fa_base_scores, fa_base_softmax and fa_base_pv on
+ * `stream` (three launches), with S and P in the caller's workspace
+ * (256-byte aligned, at least fa_base_workspace_bytes()).
+ *   in : Q, K, V bf16 (B,H,N,d)     out: O bf16 (B,H,N,d), LSE fp32 (B,H,N)
+ * Returns FA_ERR_WORKSPACE for a missing or short workspace. */
+int fa_base_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                void* workspace, size_t workspace_bytes,
+                int B, int H, int N, int d, int causal, float scale, void* stream);
+
+/* The three steps of fa_base_fwd, exposed so that each can be timed:
+ *   fa_base_scores : S = fl32(fl32(Q K^T) * scale) into S (fp32, 16-byte
+ *                    aligned, (B,H,N,ld)); entries past the diagonal block
+ *                    (causal) and past column N are not written
+ *   fa_base_softmax: P (bf16, (B,H,N,ld), 16-byte aligned) and LSE from S;
+ *                    P is written for every key the PV step reads, zeros past
+ *                    the row's last visible key
+ *   fa_base_pv     : O = bf16(P V) */
+int fa_base_scores(const void* Q, const void* K, float* S,
+                   int B, int H, int N, int d, int causal, float scale, void* stream);
+int fa_base_softmax(const float* S, void* P, float* LSE,
+                    int B, int H, int N, int causal, void* stream);
+int fa_base_pv(const void* P, const void* V, void* O,
+               int B, int H, int N, int d, int causal, void* stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* fa_status_string(int status);

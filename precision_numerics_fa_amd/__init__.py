@@ -13,12 +13,24 @@ not a gfx950 GPU, the calls raise.
 Tensors are torch.bfloat16, shape (B, H, N, d), contiguous, on the current
 CUDA (HIP) device; LSE is float32 (B, H, N).  fwd_ex / bwd_ex take
 torch.float16 tensors as well (the element type follows q).
+
+    o, lse = base_fwd(q, k, v, causal=True)   # unfused FP32-accumulating baseline
+
+base_fwd is the baseline attention the FlashAttention kernels are compared
+with (S and P materialised in HBM, softmax over whole rows in FP32); its three
+steps are also exposed (base_scores, base_softmax, base_pv).
 """
 from ._lib import (  # noqa: F401
     FA_BF16,
     FA_F16,
     FAError,
     attention,
+    base_fwd,
+    base_ld,
+    base_pv,
+    base_scores,
+    base_softmax,
+    base_workspace_bytes,
     bwd,
     bwd_ex,
     bwd_grads,

@@ -26,6 +26,12 @@ _SIGNATURES = {
     "fa_bwd_grads": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "fa_fwd_ex": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_ex": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_base_ld": (_I, [_I]),
+    "fa_base_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "fa_base_fwd": (_I, [_P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _P]),
+    "fa_base_scores": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
+    "fa_base_softmax": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
+    "fa_base_pv": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_stabilize_params": (None, [ctypes.POINTER(_F)] * 3),
     "fa_stabilize_params_ex": (_I, [_I] + [ctypes.POINTER(_F)] * 3),
@@ -300,6 +306,76 @@ def bwd_ex(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = N
           _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, N, d,
           int(bool(causal)), _scale(scale, d), int(bool(stabilize)), _stream())
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------- baseline attention
+
+def base_ld(N: int) -> int:
+    """Row stride (elements) of the baseline's S and P matrices."""
+    return int(load().fa_base_ld(int(N)))
+
+
+def base_workspace_bytes(B: int, H: int, N: int, d: int, causal: bool) -> int:
+    return int(load().fa_base_workspace_bytes(B, H, N, d, int(bool(causal))))
+
+
+def base_fwd(q, k, v, causal: bool = False, scale: Optional[float] = None, workspace=None):
+    """The unfused FP32-accumulating baseline attention.  Returns (O bf16, LSE fp32)."""
+    torch = _torch()
+    B, H, N, d = _shape(q)
+    dev = q.device
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check(n, t, torch.bfloat16, (B, H, N, d), dev)
+    if workspace is None:
+        workspace = torch.empty(base_workspace_bytes(B, H, N, d, causal), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    l = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    _call("fa_base_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), B, H, N, d, int(bool(causal)), _scale(scale, d), _stream())
+    return o, l
+
+
+def base_scores(q, k, causal: bool = False, scale: Optional[float] = None, s=None):
+    """S = fl32(fl32(Q K^T) * scale), fp32 (B, H, N, base_ld(N)); entries the
+    baseline never reads (causal: past the diagonal block; columns >= N) are
+    left as they were."""
+    torch = _torch()
+    B, H, N, d = _shape(q)
+    _check("k", k, torch.bfloat16, (B, H, N, d), q.device)
+    _check("q", q, torch.bfloat16, (B, H, N, d), q.device)
+    s = torch.empty((B, H, N, base_ld(N)), dtype=torch.float32, device=q.device) if s is None else s
+    _check("s", s, torch.float32, (B, H, N, base_ld(N)), q.device)
+    _call("fa_base_scores", _ptr(q), _ptr(k), _ptr(s), B, H, N, d, int(bool(causal)), _scale(scale, d), _stream())
+    return s
+
+
+def base_softmax(s, causal: bool = False, p=None, lse=None):
+    """P (bf16, same shape as S) and LSE (fp32 (B, H, N)) from the baseline's S."""
+    torch = _torch()
+    if s.dim() != 4:
+        raise ValueError("s must have shape (B, H, N, ld)")
+    B, H, N, ld = (int(x) for x in s.shape)
+    if ld != base_ld(N):
+        raise ValueError(f"s has row stride {ld}, expected {base_ld(N)}")
+    _check("s", s, torch.float32, (B, H, N, ld), s.device)
+    p = torch.empty((B, H, N, ld), dtype=torch.bfloat16, device=s.device) if p is None else p
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=s.device) if lse is None else lse
+    _check("p", p, torch.bfloat16, (B, H, N, ld), s.device)
+    _check("lse", lse, torch.float32, (B, H, N), s.device)
+    _call("fa_base_softmax", _ptr(s), _ptr(p), _ptr(lse), B, H, N, int(bool(causal)), _stream())
+    return p, lse
+
+
+def base_pv(p, v, causal: bool = False, out=None):
+    """O = bf16(P V) of the baseline."""
+    torch = _torch()
+    B, H, N, d = _shape(v)
+    _check("v", v, torch.bfloat16, (B, H, N, d), v.device)
+    _check("p", p, torch.bfloat16, (B, H, N, base_ld(N)), v.device)
+    o = torch.empty_like(v) if out is None else out
+    _check("out", o, torch.bfloat16, (B, H, N, d), v.device)
+    _call("fa_base_pv", _ptr(p), _ptr(v), _ptr(o), B, H, N, d, int(bool(causal)), _stream())
+    return o
 
 
 # ---------------------------------------------------------------- autograd

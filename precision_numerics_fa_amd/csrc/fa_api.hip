@@ -96,6 +96,27 @@ int bwd_impl(int dtype, const void* Q, const void* K, const void* V, const void*
   return launched(fa::launch_bwd_grads(a, s));
 }
 
+// The baseline's extra limits: rows of at most kBaseMaxN keys (its softmax
+// holds a row in registers) and one softmax workgroup per row.
+int check_base_shape(int B, int H, int N, int d) {
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (N > fa::kBaseMaxN) return FA_ERR_UNSUPPORTED;
+  if ((long double)B * H * N >= 2147483647.0L) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+size_t base_matrix_elems(int B, int H, int N) { return (size_t)B * H * N * (size_t)fa::base_ld(N); }
+
+size_t base_p_offset(int B, int H, int N) {
+  return (base_matrix_elems(B, H, N) * sizeof(float) + 255) & ~(size_t)255;
+}
+
+fa::BaseArgs base_args(const void* Q, const void* K, const void* V, void* O, float* LSE, float* S, void* P, int B,
+                       int H, int N, int d, int causal, float scale) {
+  return fa::BaseArgs{Q, K, V, O, LSE, S, P, B, H, N, d, fa::base_ld(N), causal != 0, scale};
+}
+
 }  // namespace
 
 extern "C" {
@@ -189,11 +210,75 @@ int fa_bwd_ex(int dtype, const void* Q, const void* K, const void* V, const void
                   stabilize, stream);
 }
 
+int fa_base_ld(int N) { return N < 1 ? 0 : fa::base_ld(N); }
+
+size_t fa_base_workspace_bytes(int B, int H, int N, int d, int causal) {
+  (void)causal;
+  if (check_base_shape(B, H, N, d) != FA_OK) return 0;
+  const size_t bytes = base_p_offset(B, H, N) + base_matrix_elems(B, H, N) * 2;
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int fa_base_scores(const void* Q, const void* K, float* S, int B, int H, int N, int d, int causal, float scale,
+                   void* stream) {
+  int st = check_base_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(S, 16)) return FA_ERR_INVALID_ARG;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if ((st = check_device()) != FA_OK) return st;
+  const fa::BaseArgs a = base_args(Q, K, nullptr, nullptr, nullptr, S, nullptr, B, H, N, d, causal, scale);
+  (void)hipGetLastError();
+  return launched(fa::launch_base_scores(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_base_softmax(const float* S, void* P, float* LSE, int B, int H, int N, int causal, void* stream) {
+  int st = check_base_shape(B, H, N, 64);
+  if (st != FA_OK) return st;
+  if (!aligned(S, 16) || !aligned(P, 16) || !aligned(LSE, 4)) return FA_ERR_INVALID_ARG;
+  if ((st = check_device()) != FA_OK) return st;
+  const fa::BaseArgs a =
+      base_args(nullptr, nullptr, nullptr, nullptr, LSE, const_cast<float*>(S), P, B, H, N, 64, causal, 1.0f);
+  (void)hipGetLastError();
+  return launched(fa::launch_base_softmax(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_base_pv(const void* P, const void* V, void* O, int B, int H, int N, int d, int causal, void* stream) {
+  int st = check_base_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned(P, 16) || !aligned(V, 16) || !aligned(O, 16)) return FA_ERR_INVALID_ARG;
+  if ((st = check_device()) != FA_OK) return st;
+  const fa::BaseArgs a =
+      base_args(nullptr, nullptr, V, O, nullptr, nullptr, const_cast<void*>(P), B, H, N, d, causal, 1.0f);
+  (void)hipGetLastError();
+  return launched(fa::launch_base_pv(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_base_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, void* workspace,
+                size_t workspace_bytes, int B, int H, int N, int d, int causal, float scale, void* stream) {
+  int st = check_base_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 4))
+    return FA_ERR_INVALID_ARG;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (workspace == nullptr || !aligned(workspace, 256) ||
+      workspace_bytes < fa_base_workspace_bytes(B, H, N, d, causal))
+    return FA_ERR_WORKSPACE;
+  if ((st = check_device()) != FA_OK) return st;
+  float* S = static_cast<float*>(workspace);
+  void* P = static_cast<char*>(workspace) + base_p_offset(B, H, N);
+  const fa::BaseArgs a = base_args(Q, K, V, O, LSE, S, P, B, H, N, d, causal, scale);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if ((st = launched(fa::launch_base_scores(a, s))) != FA_OK) return st;
+  if ((st = launched(fa::launch_base_softmax(a, s))) != FA_OK) return st;
+  return launched(fa::launch_base_pv(a, s));
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size, or bad scale)";
-    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (d must be 64 or 128)";
+    case FA_ERR_UNSUPPORTED: return "unsupported shape (d must be 64 or 128; the baseline takes N <= 16384)";
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_bwd_workspace_bytes()";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_DEVICE: return "current device is not a gfx950 GPU, or a device query failed";

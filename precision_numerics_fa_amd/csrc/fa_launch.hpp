@@ -54,6 +54,29 @@ hipError_t launch_bwd_grads(const BwdArgs& a, hipStream_t stream);
 // scale into the base-2 exponent).
 float scale_log2e(float scale);
 
+// The unfused baseline attention (fa_base.hip): the FP32 score matrix S and
+// the BF16 probability matrix P are (B, H, N, ld) with ld = base_ld(N).
+struct BaseArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* s;
+  void* p;
+  int B, H, N, d, ld;
+  bool causal;
+  float scale;
+};
+
+// Longest row the baseline's softmax keeps in registers (keys per row).
+constexpr int kBaseMaxN = 16384;
+
+int base_ld(int N);
+hipError_t launch_base_scores(const BaseArgs& a, hipStream_t stream);
+hipError_t launch_base_softmax(const BaseArgs& a, hipStream_t stream);
+hipError_t launch_base_pv(const BaseArgs& a, hipStream_t stream);
+
 constexpr int kFwdBlockQ = 128;
 constexpr int kFwdBlockK = 64;
 

@@ -118,3 +118,35 @@ def test_no_gpu_means_an_error_not_a_fallback(lib):
     for dt in (fa.FA_BF16, fa.FA_F16):
         assert lib.fa_fwd_ex(dt, GOOD, GOOD, GOOD, GOOD, GOOD, None, 1, 1, 64, 64, 0, 0.125, 0, None) == -5
         assert lib.fa_bwd_ex(dt, *[GOOD] * 10, need, 1, 1, 64, 64, 0, 0.125, 0, None) == -5
+    bneed = fa.base_workspace_bytes(1, 1, 64, 64, False)
+    assert lib.fa_base_fwd(*[GOOD] * 6, bneed, 1, 1, 64, 64, 0, 0.125, None) == -5
+    assert lib.fa_base_scores(*[GOOD] * 3, 1, 1, 64, 64, 0, 0.125, None) == -5
+    assert lib.fa_base_softmax(*[GOOD] * 3, 1, 1, 64, 0, None) == -5
+    assert lib.fa_base_pv(*[GOOD] * 3, 1, 1, 64, 64, 0, None) == -5
+
+
+def test_baseline_sizes_and_validation(lib):
+    """fa_base_*: the row stride, the workspace size (S fp32 then P bf16, each
+    (B,H,N,ld), P at a 256-byte boundary), the N limit of its softmax, and
+    argument checks before any device work."""
+    assert [fa.base_ld(n) for n in (1, 63, 64, 65, 4096)] == [64, 64, 64, 128, 4096]
+    assert lib.fa_base_ld(0) == 0
+    s_bytes = 2 * 3 * 100 * 128 * 4
+    assert fa.base_workspace_bytes(2, 3, 100, 64, True) == (s_bytes + 255) // 256 * 256 + 2 * 3 * 100 * 128 * 2
+    assert fa.base_workspace_bytes(1, 1, 16384, 64, False) > 0
+    assert fa.base_workspace_bytes(1, 1, 16385, 64, False) == 0
+    assert fa.base_workspace_bytes(1, 1, 64, 96, False) == 0
+    need = fa.base_workspace_bytes(1, 1, 64, 64, False)
+    base = lambda *a: lib.fa_base_fwd(*a)  # noqa: E731
+    assert base(GOOD, GOOD, GOOD, GOOD, GOOD, None, need, 1, 1, 64, 64, 0, 0.125, None) == -3
+    assert base(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, need - 1, 1, 1, 64, 64, 0, 0.125, None) == -3
+    assert base(GOOD, GOOD, GOOD, GOOD, GOOD, P(4096 + 16), need, 1, 1, 64, 64, 0, 0.125, None) == -3
+    assert base(None, GOOD, GOOD, GOOD, GOOD, GOOD, need, 1, 1, 64, 64, 0, 0.125, None) == -1
+    assert base(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, need, 1, 1, 20000, 64, 0, 0.125, None) == -2
+    assert base(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, need, 1, 1, 64, 80, 0, 0.125, None) == -2
+    assert base(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, need, 1, 1, 64, 64, 0, 0.0, None) == -1
+    assert lib.fa_base_scores(GOOD, GOOD, P(4100), 1, 1, 64, 64, 0, 0.125, None) == -1
+    assert lib.fa_base_softmax(GOOD, P(4098), GOOD, 1, 1, 64, 0, None) == -1
+    assert lib.fa_base_softmax(GOOD, GOOD, GOOD, 1, 1, 16385, 0, None) == -2
+    assert lib.fa_base_pv(GOOD, GOOD, None, 1, 1, 64, 64, 0, None) == -1
+    assert lib.fa_base_softmax(GOOD, GOOD, GOOD, 1 << 16, 1 << 10, 1 << 6, 0, None) == -1   # B*H*N >= 2^31

@@ -1,0 +1,201 @@
+"""GPU parity of the unfused FP32-accumulating baseline (fa_base_*, through the
+C ABI) against the CPU oracle.
+
+* Each step is checked on its own where its result is exact: the score
+  kernel on integer-valued inputs (every dot product exact in FP32, so S must
+  equal fl32(t * scale) bit for bit on every entry the softmax reads); the PV
+  kernel on probabilities and values whose products and sums are exact.
+* The softmax step, fed the GPU's own S, against the baseline emulation's
+  softmax of the same S: its row sum is reduced in a different order, so a
+  few probabilities may land one bf16 ulp away; the rest are bit-identical,
+  and P is zero on every key past the row's last visible one that the PV
+  step reads.
+* The whole baseline against the exact oracle (the forward's gates) and
+  against the baseline emulation, on ragged shapes; at full Llama-2-7B shape
+  on sampled heads.
+* The hand-derived three-way-tie example: the baseline's bf16(1/3)
+  probabilities give 2.34375 where FlashAttention (fix off or on) gives the
+  correctly rounded 2.328125.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import fa_inputs as F
+from oracle import baseline as BASE
+from oracle import emulation as EMU
+from oracle import metrics as Mt
+from oracle import reference as REF
+
+from gpu_util import device_inputs, head_f64, random_case, say, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 1.5e-2
+MEAN_ABS = 2e-3
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+    import precision_numerics_fa_amd as fa
+    assert torch.cuda.is_available()
+    fa.load()
+    return fa
+
+
+def _visible(N, causal):
+    return np.tril(np.ones((N, N), dtype=bool)) if causal else np.ones((N, N), dtype=bool)
+
+
+def _pv_read_width(N, ld, causal):
+    """Per row, the keys the PV step reads: to the end of the row's 64-key
+    block (causal) or the whole padded row."""
+    if not causal:
+        return np.full(N, ld)
+    return np.minimum(ld, 64 * (np.arange(N) // 64 + 1))
+
+
+SHAPES = [(1, 1, 1, 64), (1, 2, 17, 64), (2, 1, 129, 128), (1, 3, 200, 64), (2, 2, 333, 128), (1, 1, 64, 128)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N,d", SHAPES)
+def test_scores_exact_on_integer_inputs(fa, B, H, N, d, causal):
+    import torch
+    say(f"base scores B={B} H={H} N={N} d={d} causal={causal}")
+    rng = np.random.default_rng(N * 3 + d)
+    qi = rng.integers(-3, 4, (B, H, N, d)).astype(np.float32)
+    ki = rng.integers(-3, 4, (B, H, N, d)).astype(np.float32)
+    q = torch.from_numpy(qi).to(torch.bfloat16).cuda()
+    k = torch.from_numpy(ki).to(torch.bfloat16).cuda()
+    scale = 1.0 / np.sqrt(d)
+    s = fa.base_scores(q, k, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    s = s.cpu().numpy().astype(np.float64)[..., :N]
+    ref = BASE.scores(qi.astype(np.float64), ki.astype(np.float64), scale, causal)
+    vis = np.broadcast_to(_visible(N, causal), ref.shape)
+    assert np.array_equal(s[vis], ref[vis])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N,d", SHAPES)
+def test_softmax_against_emulation_on_the_same_scores(fa, B, H, N, d, causal):
+    import torch
+    say(f"base softmax B={B} H={H} N={N} d={d} causal={causal}")
+    bits, dev = random_case(B, H, N, d, seed=N + 5 * d + B, mult=2.0)
+    s = fa.base_scores(dev["q"], dev["k"], causal=causal)
+    p, lse = fa.base_softmax(s, causal=causal)
+    torch.cuda.synchronize()
+    ld = fa.base_ld(N)
+    s_host = s.cpu().numpy().astype(np.float64)[..., :N]
+    s_host = np.where(_visible(N, causal), s_host, -np.inf)
+    p_ref, lse_ref = BASE.softmax(s_host)
+    p_gpu = to_f64(p)
+    width = _pv_read_width(N, ld, causal)
+    cols = np.arange(ld)[None, :]
+    written = (cols < width[:, None])[:, :N]      # P past the PV step's read range is not written
+    pg = p_gpu[..., :N][..., written]
+    pr = p_ref[..., written]
+    assert np.isfinite(pg).all()
+    assert (pg == pr).mean() >= 0.99, (pg == pr).mean()
+    assert (np.abs(pg - pr) <= Mt.bf16_ulp(pr)).all()
+    last_visible = np.arange(N) + 1 if causal else np.full(N, N)
+    beyond = (cols >= last_visible[:, None]) & (cols < width[:, None])
+    assert (p_gpu[..., beyond] == 0).all()
+    assert np.abs(to_f64(lse) - lse_ref).max() <= 2e-6 * max(1.0, np.abs(lse_ref).max())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N,d", SHAPES)
+def test_pv_exact_on_exact_products(fa, B, H, N, d, causal):
+    """P entries are multiples of 1/64 below 1 and V entries small integers:
+    every product and partial sum is exact in FP32, so O = bf16(P V) exactly."""
+    import torch
+    say(f"base pv B={B} H={H} N={N} d={d} causal={causal}")
+    ld = fa.base_ld(N)
+    rng = np.random.default_rng(N + d + 11)
+    p = rng.integers(0, 64, (B, H, N, ld)).astype(np.float32) / 64.0
+    width = _pv_read_width(N, ld, causal)
+    vis = np.zeros((N, ld), dtype=bool)
+    vis[:, :N] = _visible(N, causal)
+    p = np.where(vis, p, 0.0).astype(np.float32)
+    p_pad = np.where(np.arange(ld)[None, :] < width[:, None], p, np.float32(7.0))  # never read
+    v = rng.integers(-4, 5, (B, H, N, d)).astype(np.float32)
+    o = fa.base_pv(torch.from_numpy(p_pad).to(torch.bfloat16).cuda(), torch.from_numpy(v).to(torch.bfloat16).cuda(),
+                   causal=causal)
+    torch.cuda.synchronize()
+    ref = EMU.bf16(p[..., :N].astype(np.float64) @ v.astype(np.float64))
+    assert np.array_equal(to_f64(o), ref)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N,d", SHAPES + [(1, 2, 1000, 128), (2, 2, 511, 64)])
+def test_baseline_against_oracles(fa, B, H, N, d, causal):
+    say(f"base fwd B={B} H={H} N={N} d={d} causal={causal}")
+    bits, dev = random_case(B, H, N, d, seed=3 * N + d + B)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = fa.base_fwd(dev["q"], dev["k"], dev["v"], causal=causal)
+    q, k, v = (head_f64(bits[n]) for n in ("q", "k", "v"))
+    o_ref, lse_ref = REF.forward(q, k, v, scale, causal)
+    og = to_f64(o)
+    e = Mt.output_errors(og, o_ref)
+    assert e["max_abs"] <= MAX_ABS and e["mean_abs"] <= MEAN_ABS and e["finite"], e
+    assert np.abs(to_f64(lse) - lse_ref).max() <= 1e-4
+    o_emu, _ = BASE.forward(q, k, v, scale, causal)
+    assert (og == o_emu).mean() >= 0.97, (og == o_emu).mean()
+    # the three steps through their own entry points compose to fa_base_fwd
+    # bit for bit, and the PV step on the GPU's own P is the FP32-accumulated
+    # product to one bf16 ulp (the summation order is the only difference;
+    # against the emulation's P a probability one ulp apart can move O by more)
+    s_ = fa.base_scores(dev["q"], dev["k"], causal=causal)
+    p_, _ = fa.base_softmax(s_, causal=causal)
+    o2 = fa.base_pv(p_, dev["v"], causal=causal)
+    assert np.array_equal(to_f64(o2), og)
+    p_read = np.where(_visible(N, causal), to_f64(p_)[..., :N], 0.0)   # P past the read range is not written
+    pv_ref = EMU.bf16(EMU.fl32(p_read @ v))
+    # one bf16 ulp of the result, plus an FP32 accumulation allowance of 2^-20
+    # times sum |P| |V| (it matters only where the sum cancels to near zero)
+    bound = Mt.bf16_ulp(pv_ref) + 2.0 ** -20 * (np.abs(p_read) @ np.abs(v))
+    assert (np.abs(og - pv_ref) <= bound).all()
+
+
+def test_golden_three_way_tie_on_gpu(fa):
+    import torch
+    with open(os.path.join(GOLDEN, "baseline_three_way_tie.json")) as f:
+        g = json.load(f)
+    d = 64
+    pad = lambda a: np.pad(np.array(a, dtype=np.float32), ((0, 0), (0, d - len(a[0]))))[None, None]  # noqa: E731
+    q, k, v = (torch.from_numpy(pad(g[n])).to(torch.bfloat16).cuda() for n in ("q", "k", "v"))
+    q = q.expand(1, 1, 3, d).contiguous()   # three queries, all seeing the three tied keys
+    o, lse = fa.base_fwd(q, k, v, causal=False, scale=g["scale"])
+    og = to_f64(o)[0, 0]
+    assert (og[:, :2] == np.array(g["o_baseline"])).all() and (og[:, 2:] == 0).all()
+    assert np.abs(to_f64(lse) - g["lse"]).max() < 1e-6
+    for stab in (False, True):
+        o_fa, _ = fa.fwd(q, k, v, causal=False, scale=g["scale"], stabilize=stab)
+        assert (to_f64(o_fa)[0, 0, :, :2] == np.array(g["o_flash"])).all()
+
+
+@pytest.mark.parametrize("stabilize", [False, True])
+def test_c4_full_baseline_and_flash_on_sampled_heads(fa, stabilize):
+    """Llama-2-7B shape (4, 32, 4096, 128), causal: the baseline and
+    FlashAttention in the launch configuration the benchmark times, both
+    against the exact oracle on seeded heads."""
+    import torch
+    w = F.WORKLOADS["c4"]
+    say(f"base c4 full stabilize={stabilize}")
+    full, dev = device_inputs(w)
+    o_b, _ = fa.base_fwd(dev["q"], dev["k"], dev["v"], causal=True)
+    o_f, _ = fa.fwd(dev["q"], dev["k"], dev["v"], causal=True, stabilize=stabilize)
+    torch.cuda.synchronize()
+    scale = 1.0 / np.sqrt(w.d)
+    for b, h in F.sample_pairs(w, 3, seed=int(stabilize) + 7):
+        q, k, v = (head_f64(full[n][b, h]) for n in ("q", "k", "v"))
+        o_ref, _ = REF.forward(q, k, v, scale, True)
+        for name, o in (("baseline", o_b), ("flash", o_f)):
+            e = Mt.output_errors(to_f64(o[b, h]), o_ref)
+            assert e["max_abs"] <= MAX_ABS and e["mean_abs"] <= MEAN_ABS, (name, b, h, e)
