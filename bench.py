@@ -2,9 +2,14 @@
 
 One step = one full pass of the hot path on the Llama-2-7B attention shape
 (B=4, H=32, N=4096, d=128, causal, stabilised shift on): fa_fwd, then the
-backward's three kernels (row-dot prepass, dK/dV, dQ).  Inputs are resident in
-HBM before the timed region.  The step is timed as a whole (synchronised wall
-clock) and each kernel with HIP events on the stream it is launched on.
+backward's two launches (row-dot prepass, then dQ/dK/dV in one launch).  Inputs
+are resident in HBM before the timed region.  The step is timed as a whole
+(synchronised wall clock) and each kernel with HIP events on the stream it is
+launched on.  Outside the timed step, the same inputs also go through the
+unfused FP32-accumulating baseline attention (fa_base_*: its three kernels
+timed against the HBM roofline), and FlashAttention (fix on and off) and the
+baseline are compared with the float64 oracle on the same heads (page 3's
+deviation comparison).
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
     python bench.py --sweep [--steps 20]      # per-workload forward/backward table
@@ -248,9 +253,73 @@ def main():
     }
 
     out["f16"] = f16_leg(args, fwd_flop, bwd_flop)
+    o_plain = torch.empty_like(q)
+    fa.fwd(q, k, v, causal=True, stabilize=False, out=o_plain, lse=torch.empty_like(lse))
+    base = baseline_leg(args, q, k, v, fwd_flop, kern_ms["fwd"])
+    out["baseline_fp32acc"] = base.pop("record")
     if not args.no_cpu_baseline:
-        out.update(cpu_baseline_leg(w, full, o, lse, dq, dk, dv, args.cpu_heads, fwd_flop + bwd_flop))
+        out.update(cpu_baseline_leg(w, full, o, lse, dq, dk, dv, args.cpu_heads, fwd_flop + bwd_flop,
+                                    compare={"flash_fix_on": o, "flash_fix_off": o_plain,
+                                             "baseline_fp32acc": base["o"]}))
     print(json.dumps(out), flush=True)
+
+
+def baseline_leg(args, q, k, v, fwd_flop, fa_fwd_ms):
+    """The unfused FP32-accumulating baseline on the same inputs: each of its
+    three launches timed with HIP events, against the HBM roofline with the
+    bytes the algorithm must move (Q, K in and the visible scores out; the
+    scores in and the probabilities out; the probabilities and V in and O
+    out).  Returns the record and the baseline's O for the deviation study."""
+    import torch
+
+    import precision_numerics_fa_amd as fa
+
+    B, H, N, d = (int(x) for x in q.shape)
+    ld = fa.base_ld(N)
+    S = torch.empty((B, H, N, ld), dtype=torch.float32, device="cuda")
+    P = torch.empty((B, H, N, ld), dtype=torch.bfloat16, device="cuda")
+    ob = torch.empty_like(q)
+    lb = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    steps = [("scores", lambda: fa.base_scores(q, k, causal=True, s=S)),
+             ("softmax", lambda: fa.base_softmax(S, causal=True, p=P, lse=lb)),
+             ("pv", lambda: fa.base_pv(P, v, causal=True, out=ob))]
+    reps = max(3, args.steps // 5)
+    for _ in range(2):
+        for _, fn in steps:
+            fn()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for r in range(reps):
+        for i, (_, fn) in enumerate(steps):
+            ev[r][i].record()
+            fn()
+        ev[r][3].record()
+    torch.cuda.synchronize()
+    ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in ev) / reps for i, (n, _) in enumerate(steps)}
+    vis = B * H * N * (N + 1) // 2          # causal scores
+    elem = B * H * N * d
+    algo = {"scores": 2 * elem * 2 + vis * 4, "softmax": vis * 4 + vis * 2 + B * H * N * 4,
+            "pv": vis * 2 + elem * 2 + elem * 2}
+    names = {"scores": "base_scores_kernel", "softmax": "base_softmax_kernel", "pv": "base_pv_kernel"}
+    kernels = {}
+    for n in ms:
+        ach = algo[n] / (ms[n] * 1e-3) / 1e9
+        kernels[n] = {"kernel": names[n], "ms": round(ms[n], 4), "bound": "hbm", "achieved": round(ach, 1),
+                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                      "bytes": algo[n]}
+    total = sum(ms.values())
+    # the same call through the one-shot entry point, bitwise the steps' result
+    ob2, _ = fa.base_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ob, ob2))
+    del S, P, ob2
+    torch.cuda.empty_cache()
+    rec = {"workload": f"same inputs (B={B} H={H} N={N} d={d}, causal): unfused baseline attention with FP32 "
+                       "accumulation, S (fp32) and P (bf16) materialised in HBM",
+           "ms": round(total, 4), "tflops": round(fwd_flop / (total * 1e-3) / 1e12, 1),
+           "flash_fwd_speedup": round(total / fa_fwd_ms, 2), "kernels": kernels,
+           "one_shot_equals_steps": same}
+    return {"record": rec, "o": ob}
 
 
 def f16_leg(args, fwd_flop, bwd_flop):
@@ -331,6 +400,12 @@ def sweep(args):
         t_on = min(t_on, *(_timed(fon, reps) for _ in range(2)))
         fon()
         t_bwd = min(_timed(bwd, reps) for _ in range(3))
+        t_base = None
+        if w.dtype == "bf16":
+            ws = torch.empty(fa.base_workspace_bytes(B, H, N, d, w.causal), dtype=torch.uint8, device="cuda")
+            base = lambda: fa.base_fwd(q, k, v, causal=w.causal, workspace=ws)  # noqa: E731
+            t_base = min(_timed(base, reps) for _ in range(2))
+            del ws
         pairs = N * (N + 1) / 2 if w.causal else N * N
         fwd_flop = 4.0 * B * H * pairs * d
         elem = B * H * N * d
@@ -344,14 +419,20 @@ def sweep(args):
                "bwd_ms": round(t_bwd, 4),
                "bwd_tflops": round(2.5 * fwd_flop / (t_bwd * 1e-3) / 1e12, 1),
                "bwd_pct_peak": round(100 * 2.5 * fwd_flop / (t_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+        if t_base is not None:
+            rec["baseline_fp32acc_ms"] = round(t_base, 4)
+            rec["flash_speedup_over_baseline"] = round(t_base / t_on, 2)
         print(json.dumps(rec), flush=True)
         del dev, q, k, v, do, res
         torch.cuda.empty_cache()
 
 
-def cpu_baseline_leg(w, full, o, lse, dq, dk, dv, heads, step_flop):
+def cpu_baseline_leg(w, full, o, lse, dq, dk, dv, heads, step_flop, compare=None):
     """Time the float64 oracle on a few heads of the same workload, and check
-    the GPU's outputs for those heads against it."""
+    the GPU's outputs for those heads against it.  ``compare`` maps names to
+    further GPU outputs of the same forward (FlashAttention with the fix on and
+    off, the FP32-accumulating baseline), whose deviation from the exact
+    result is reported side by side on the same heads (page 3's comparison)."""
     import platform
 
     import numpy as np
@@ -364,6 +445,7 @@ def cpu_baseline_leg(w, full, o, lse, dq, dk, dv, heads, step_flop):
     pairs = F.sample_pairs(w, heads, seed=7)
     f64 = lambda b: F.bf16_bits_to_f32(b).astype(np.float64)  # noqa: E731
     t_cpu = 0.0
+    dev_stats = {}
     errs = {"max_abs": 0.0, "mean_abs": [], "max_rel_normwise": 0.0, "dq": 0.0, "dk": 0.0, "dv": 0.0,
             "lse_max_abs": 0.0}
     for (b, h) in pairs:
@@ -379,11 +461,29 @@ def cpu_baseline_leg(w, full, o, lse, dq, dk, dv, heads, step_flop):
         errs["lse_max_abs"] = max(errs["lse_max_abs"], float(np.abs(lse[b, h].cpu().numpy() - lse_ref).max()))
         for n, g, r in (("dq", dq, g_ref[0]), ("dk", dk, g_ref[1]), ("dv", dv, g_ref[2])):
             errs[n] = max(errs[n], Mt.relative_fro(g[b, h].float().cpu().numpy(), r))
+        for name, oc in (compare or {}).items():
+            ec = Mt.output_errors(oc[b, h].float().cpu().numpy(), o_ref)
+            dv_ = dev_stats.setdefault(name, {"max_abs": 0.0, "mean_abs": [], "max_rel_normwise": 0.0,
+                                              "max_rel_rowwise": 0.0})
+            for key_ in ("max_abs", "max_rel_normwise", "max_rel_rowwise"):
+                dv_[key_] = max(dv_[key_], ec[key_])
+            dv_["mean_abs"].append(ec["mean_abs"])
     errs["mean_abs"] = float(np.mean(errs["mean_abs"]))
     per_head_flop = step_flop / (w.B * w.H)
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     cpu_tflops = per_head_flop * len(pairs) / t_cpu / 1e12
+    for dv_ in dev_stats.values():
+        dv_["mean_abs"] = float(np.mean(dv_["mean_abs"]))
+    deviation = None
+    if dev_stats:
+        deviation = {"heads": len(pairs), "against": "float64 oracle (exact attention)", **dev_stats}
+        if "baseline_fp32acc" in dev_stats and "flash_fix_off" in dev_stats:
+            b_, f_ = dev_stats["baseline_fp32acc"], dev_stats["flash_fix_off"]
+            deviation["flash_over_baseline"] = {
+                k_: round(f_[k_] / b_[k_], 3) for k_ in ("max_abs", "mean_abs", "max_rel_normwise",
+                                                         "max_rel_rowwise") if b_[k_] > 0}
     return {
+        "deviation_study": deviation,
         "cpu_baseline": {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": int(threads),
                          "kind": "oracle",
                          "sample": f"float64 oracle forward+backward on {len(pairs)} of {w.B * w.H} heads "
