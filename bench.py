@@ -220,6 +220,10 @@ def main():
         kernels[n]["traffic"] = counter_traffic(kernel_names[n])
         if kflop[n] > 0:
             kernels[n]["mfma_pipe_busy"] = counter_mfma_busy(kernel_names[n])
+    peaks = measured_peaks()
+    for n in names:
+        meas = peaks["mfma_bf16_tflops"] if kernels[n]["bound"] == "mfma" else peaks["hbm_copy_gbs"]
+        kernels[n]["frac_of_measured"] = round(kernels[n]["achieved"] / meas, 4)
     dominant = max(names, key=lambda n: kern_ms[n])
     roofline = dict(kernels[dominant])
     roofline.pop("ms")
@@ -249,6 +253,7 @@ def main():
         "fwd_stabilize_on_ms": round(kern_ms["fwd"], 4),
         "kernels": kernels,
         "roofline": roofline,
+        "measured_peaks": peaks,
         "input_gen_s": round(gen_s, 2),
     }
 
@@ -262,6 +267,32 @@ def main():
                                     compare={"flash_fix_on": o, "flash_fix_off": o_plain,
                                              "baseline_fp32acc": base["o"]}))
     print(json.dumps(out), flush=True)
+
+
+def measured_peaks():
+    """The ceilings this chip sustains, measured in the same run: dense bf16
+    MFMA throughput from the library's probe kernel (register operands only),
+    and HBM bandwidth from a 1 GiB device-to-device copy (read + write bytes).
+    Each is the best of five timed launches."""
+    import torch
+
+    import precision_numerics_fa_amd as fa
+
+    out = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    flop, _ = fa.mfma_probe(2048, 2000, out=out)
+    fa.mfma_probe(2048, 2000, out=out)
+    t_mfma = min(_timed(lambda: fa.mfma_probe(2048, 2000, out=out), 1) for _ in range(5))
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    t_copy = min(_timed(lambda: dst.copy_(src), 1) for _ in range(5))
+    nbytes = 2 * src.numel() * 4
+    del src, dst, out
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": round(flop / (t_mfma * 1e-3) / 1e12, 1),
+            "hbm_copy_gbs": round(nbytes / (t_copy * 1e-3) / 1e9, 1),
+            "how": "bf16 MFMA-only probe kernel (2048 workgroups, 8 chains per wave); 1 GiB device copy, "
+                   "read+write bytes; best of 5"}
 
 
 def baseline_leg(args, q, k, v, fwd_flop, fa_fwd_ms):
@@ -474,6 +505,13 @@ def cpu_baseline_leg(w, full, o, lse, dq, dk, dv, heads, step_flop, compare=None
     cpu_tflops = per_head_flop * len(pairs) / t_cpu / 1e12
     for dv_ in dev_stats.values():
         dv_["mean_abs"] = float(np.mean(dv_["mean_abs"]))
+    # oracle B (the bf16 blocked emulation of the forward) on one of the heads
+    from oracle import emulation as EMU
+    b0, h0 = pairs[0]
+    q0, k0, v0 = (f64(full[n][b0, h0]) for n in ("q", "k", "v"))
+    t0 = time.perf_counter()
+    EMU.forward(q0, k0, v0, w.scale, w.causal, stabilize=True)
+    t_emu = time.perf_counter() - t0
     deviation = None
     if dev_stats:
         deviation = {"heads": len(pairs), "against": "float64 oracle (exact attention)", **dev_stats}
@@ -489,7 +527,8 @@ def cpu_baseline_leg(w, full, o, lse, dq, dk, dv, heads, step_flop, compare=None
                          "sample": f"float64 oracle forward+backward on {len(pairs)} of {w.B * w.H} heads "
                                    f"(N={w.N}, d={w.d}, causal), {t_cpu:.1f} s; TFLOP/s under the "
                                    f"GPU's algorithmic FLOP count",
-                         "cpu": platform.processor() or platform.machine(), "seconds": round(t_cpu, 2)},
+                         "cpu": platform.processor() or platform.machine(), "seconds": round(t_cpu, 2),
+                         "oracle_b_forward_s_per_head": round(t_emu, 2)},
         "accuracy": {"heads_checked": len(pairs), "o_max_abs": errs["max_abs"], "o_mean_abs": errs["mean_abs"],
                      "o_max_rel_normwise": errs["max_rel_normwise"], "lse_max_abs": errs["lse_max_abs"],
                      "dq_rel": errs["dq"], "dk_rel": errs["dk"], "dv_rel": errs["dv"]},

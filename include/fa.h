@@ -206,6 +206,18 @@ int fa_base_softmax(const float* S, void* P, float* LSE,
 int fa_base_pv(const void* P, const void* V, void* O,
                int B, int H, int N, int d, int causal, void* stream);
 
+/* Measured MFMA ceiling (reporting only): launches `blocks` workgroups of
+ * four waves that each run `iters` rounds of eight independent
+ * v_mfma_f32_32x32x16_bf16 chains on register operands (the product
+ * instruction of every attention kernel here), and writes one float per
+ * thread to `out` (blocks*256 floats, device memory) so that the work is
+ * kept.  Returns the FLOP that launch performs (> 0), or a negative status
+ * (FA_ERR_INVALID_ARG for a NULL `out` or non-positive sizes, FA_ERR_DEVICE,
+ * FA_ERR_LAUNCH).  Timing it with events on `stream` gives the dense bf16
+ * rate the chip sustains, against which the attention kernels' achieved
+ * rates are also quoted. */
+long long fa_mfma_probe(float* out, int blocks, int iters, void* stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* fa_status_string(int status);
 

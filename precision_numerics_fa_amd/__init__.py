@@ -43,6 +43,7 @@ from ._lib import (  # noqa: F401
     fwd_tile,
     lib_path,
     load,
+    mfma_probe,
     stabilize_params,
     status_string,
     version,

@@ -32,6 +32,7 @@ _SIGNATURES = {
     "fa_base_scores": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "fa_base_softmax": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_base_pv": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "fa_mfma_probe": (ctypes.c_longlong, [_P, _I, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_stabilize_params": (None, [ctypes.POINTER(_F)] * 3),
     "fa_stabilize_params_ex": (_I, [_I] + [ctypes.POINTER(_F)] * 3),
@@ -376,6 +377,20 @@ def base_pv(p, v, causal: bool = False, out=None):
     _check("out", o, torch.bfloat16, (B, H, N, d), v.device)
     _call("fa_base_pv", _ptr(p), _ptr(v), _ptr(o), B, H, N, d, int(bool(causal)), _stream())
     return o
+
+
+# ---------------------------------------------------------------- measured ceiling
+
+def mfma_probe(blocks: int = 2048, iters: int = 2000, out=None):
+    """Enqueue the bf16 MFMA throughput probe; returns (FLOP of the launch, out)."""
+    torch = _torch()
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda") if out is None else out
+    if out.numel() < blocks * 256 or out.dtype != torch.float32:
+        raise ValueError("out must hold blocks*256 float32 values")
+    flop = int(load().fa_mfma_probe(_ptr(out), int(blocks), int(iters), _stream()))
+    if flop < 0:
+        raise FAError("fa_mfma_probe", flop)
+    return flop, out
 
 
 # ---------------------------------------------------------------- autograd

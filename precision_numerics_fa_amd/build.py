@@ -26,7 +26,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_base.hip", "fa_api.hip"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_base.hip", "fa_probe.hip", "fa_api.hip"]
 ARCH = "gfx950"
 
 

@@ -274,6 +274,15 @@ int fa_base_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE
   return launched(fa::launch_base_pv(a, s));
 }
 
+long long fa_mfma_probe(float* out, int blocks, int iters, void* stream) {
+  if (out == nullptr || !aligned(out, 4) || blocks < 1 || iters < 1 || blocks > (1 << 24)) return FA_ERR_INVALID_ARG;
+  const int st = check_device();
+  if (st != FA_OK) return st;
+  (void)hipGetLastError();
+  const int ls = launched(fa::launch_mfma_probe(out, blocks, iters, static_cast<hipStream_t>(stream)));
+  return ls != FA_OK ? ls : fa::mfma_probe_flop(blocks, iters);
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";

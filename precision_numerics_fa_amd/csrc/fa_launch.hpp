@@ -77,6 +77,11 @@ hipError_t launch_base_scores(const BaseArgs& a, hipStream_t stream);
 hipError_t launch_base_softmax(const BaseArgs& a, hipStream_t stream);
 hipError_t launch_base_pv(const BaseArgs& a, hipStream_t stream);
 
+// The bf16 MFMA throughput probe (fa_probe.hip): FLOP done by one launch of
+// `blocks` workgroups of `iters` iterations, and the launch.
+long long mfma_probe_flop(int blocks, int iters);
+hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t stream);
+
 constexpr int kFwdBlockQ = 128;
 constexpr int kFwdBlockK = 64;
 

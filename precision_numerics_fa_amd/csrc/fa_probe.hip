@@ -1,0 +1,48 @@
+// Measured ceilings for the roofline figures: a kernel that does nothing but
+// bf16 MFMAs (v_mfma_f32_32x32x16_bf16, the instruction of every product in
+// the attention kernels), so that achieved TFLOP/s can be quoted against the
+// dense rate this chip sustains under load as well as against its data-sheet
+// peak.  Each wave keeps eight independent accumulator chains in flight, two
+// waves per SIMD; operands stay in registers, so neither memory nor LDS takes
+// part.  The result is written out so that the chains are not removed.
+#include "fa_device.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+namespace {
+
+constexpr int kProbeChains = 8;
+
+__global__ __launch_bounds__(256, 2) void mfma_probe_kernel(float* __restrict__ out, int iters) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = (__bf16)((float)((lane + j) & 7) * (1.0f / 1024.0f));
+    b[j] = (__bf16)((float)((lane * 3 + j) & 7) * (1.0f / 1024.0f));
+  }
+  f32x16 c[kProbeChains];
+#pragma unroll
+  for (int t = 0; t < kProbeChains; ++t) c[t] = zero16();
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int t = 0; t < kProbeChains; ++t) c[t] = mfma<__bf16>(a, b, c[t]);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int t = 0; t < kProbeChains; ++t) s += c[t][t];
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+}  // namespace
+
+long long mfma_probe_flop(int blocks, int iters) {
+  return (long long)blocks * 4 * iters * kProbeChains * (2LL * 32 * 32 * 16);
+}
+
+hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t s) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, s, out, iters);
+  return hipGetLastError();
+}
+
+}  // namespace fa

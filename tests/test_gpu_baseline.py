@@ -199,3 +199,25 @@ def test_c4_full_baseline_and_flash_on_sampled_heads(fa, stabilize):
         for name, o in (("baseline", o_b), ("flash", o_f)):
             e = Mt.output_errors(to_f64(o[b, h]), o_ref)
             assert e["max_abs"] <= MAX_ABS and e["mean_abs"] <= MEAN_ABS, (name, b, h, e)
+
+
+def test_mfma_probe_counts_its_flop_and_computes_the_product(fa):
+    """The MFMA ceiling probe: the FLOP it reports, and its result against the
+    product its operands define (small exact values, so bit-exact), which also
+    checks the operand and accumulator layouts documented in fa_device.hpp."""
+    import torch
+    blocks, iters = 8, 3
+    flop, out = fa.mfma_probe(blocks, iters)
+    torch.cuda.synchronize()
+    assert flop == blocks * 4 * iters * 8 * 2 * 32 * 32 * 16
+    lanes = np.arange(64)
+    A = np.zeros((32, 16))
+    Bm = np.zeros((16, 32))
+    for l in lanes:
+        for j in range(8):
+            A[l % 32, 8 * (l // 32) + j] = ((l + j) & 7) / 1024.0
+            Bm[8 * (l // 32) + j, l % 32] = ((3 * l + j) & 7) / 1024.0
+    C = iters * (A @ Bm)
+    expect = np.array([sum(C[8 * (t // 4) + 4 * (l // 32) + t % 4, l % 32] for t in range(8)) for l in lanes])
+    got = out.cpu().numpy().astype(np.float64).reshape(blocks * 4, 64)
+    assert np.array_equal(got, np.broadcast_to(expect, got.shape))
