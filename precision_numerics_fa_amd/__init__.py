@@ -42,6 +42,7 @@ from ._lib import (  # noqa: F401
     fwd_ex,
     fwd_tile,
     lib_path,
+    hbm_probe,
     load,
     mfma_probe,
     stabilize_params,

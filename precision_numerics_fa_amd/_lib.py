@@ -33,6 +33,7 @@ _SIGNATURES = {
     "fa_base_softmax": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_base_pv": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fa_mfma_probe": (ctypes.c_longlong, [_P, _I, _I, _P]),
+    "fa_hbm_probe": (_I, [_P, _P, _S, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_stabilize_params": (None, [ctypes.POINTER(_F)] * 3),
     "fa_stabilize_params_ex": (_I, [_I] + [ctypes.POINTER(_F)] * 3),
@@ -391,6 +392,16 @@ def mfma_probe(blocks: int = 2048, iters: int = 2000, out=None):
     if flop < 0:
         raise FAError("fa_mfma_probe", flop)
     return flop, out
+
+
+def hbm_probe(src, dst):
+    """Enqueue the HBM bandwidth probe: copy src into dst (same byte size,
+    contiguous device tensors)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous and of the same byte size")
+    _call("fa_hbm_probe", _ptr(src), _ptr(dst), nbytes, _stream())
+    return dst
 
 
 # ---------------------------------------------------------------- autograd

@@ -150,3 +150,17 @@ def test_baseline_sizes_and_validation(lib):
     assert lib.fa_base_softmax(GOOD, GOOD, GOOD, 1, 1, 16385, 0, None) == -2
     assert lib.fa_base_pv(GOOD, GOOD, None, 1, 1, 64, 64, 0, None) == -1
     assert lib.fa_base_softmax(GOOD, GOOD, GOOD, 1 << 16, 1 << 10, 1 << 6, 0, None) == -1   # B*H*N >= 2^31
+
+
+def test_probe_argument_validation(lib):
+    """The measured-ceiling probes check their arguments before any device work."""
+    assert lib.fa_mfma_probe(None, 8, 3, None) == -1
+    assert lib.fa_mfma_probe(GOOD, 0, 3, None) == -1
+    assert lib.fa_mfma_probe(GOOD, 8, 0, None) == -1
+    assert lib.fa_hbm_probe(GOOD, P(1 << 20), 100, None) == -1         # not a multiple of 16
+    assert lib.fa_hbm_probe(GOOD, P(4096 + 64), 256, None) == -1       # overlapping
+    assert lib.fa_hbm_probe(P(4100), P(1 << 20), 256, None) == -1      # misaligned
+    import torch
+    if not torch.cuda.is_available():
+        assert lib.fa_mfma_probe(GOOD, 8, 3, None) == -5
+        assert lib.fa_hbm_probe(GOOD, P(1 << 20), 256, None) == -5

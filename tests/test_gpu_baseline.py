@@ -221,3 +221,17 @@ def test_mfma_probe_counts_its_flop_and_computes_the_product(fa):
     expect = np.array([sum(C[8 * (t // 4) + 4 * (l // 32) + t % 4, l % 32] for t in range(8)) for l in lanes])
     got = out.cpu().numpy().astype(np.float64).reshape(blocks * 4, 64)
     assert np.array_equal(got, np.broadcast_to(expect, got.shape))
+
+
+def test_hbm_probe_copies(fa):
+    import torch
+    src = torch.arange(1 << 20, dtype=torch.float32, device="cuda") * 0.5 + 3.0
+    dst = torch.zeros_like(src)
+    fa.hbm_probe(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    src2 = torch.arange(12, dtype=torch.float32, device="cuda")   # 48 bytes: a tail shorter than the stride
+    dst2 = torch.zeros_like(src2)
+    fa.hbm_probe(src2, dst2)
+    torch.cuda.synchronize()
+    assert torch.equal(src2, dst2)
