@@ -218,12 +218,14 @@ int fa_base_pv(const void* P, const void* V, void* O,
  * rates are also quoted. */
 long long fa_mfma_probe(float* out, int blocks, int iters, void* stream);
 
-/* Measured HBM ceiling (reporting only): copies `bytes` (a multiple of 16)
- * from `src` to `dst` (device memory, 16-byte aligned, not overlapping) with
- * 16-byte loads and stores.  Timed with events on `stream`, 2*bytes over the
- * time is the streaming bandwidth the memory-bound kernels are compared with.
+/* Measured HBM ceiling (reporting only): reads `bytes` (a multiple of 16) of
+ * `src` (device memory, 16-byte aligned) with 16-byte loads and writes one
+ * folded value per thread to `sink` (device memory, 4096*256 unsigned ints),
+ * so that the loads are kept.  Timed with events on `stream`, bytes over the
+ * time is the streaming read bandwidth the memory-bound kernels (whose
+ * traffic is almost all reads) are compared with.
  * Returns FA_OK, FA_ERR_INVALID_ARG, FA_ERR_DEVICE or FA_ERR_LAUNCH. */
-int fa_hbm_probe(const void* src, void* dst, size_t bytes, void* stream);
+int fa_hbm_probe(const void* src, size_t bytes, unsigned int* sink, void* stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* fa_status_string(int status);

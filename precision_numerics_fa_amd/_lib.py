@@ -33,7 +33,7 @@ _SIGNATURES = {
     "fa_base_softmax": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_base_pv": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fa_mfma_probe": (ctypes.c_longlong, [_P, _I, _I, _P]),
-    "fa_hbm_probe": (_I, [_P, _P, _S, _P]),
+    "fa_hbm_probe": (_I, [_P, _S, _P, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_stabilize_params": (None, [ctypes.POINTER(_F)] * 3),
     "fa_stabilize_params_ex": (_I, [_I] + [ctypes.POINTER(_F)] * 3),
@@ -394,14 +394,21 @@ def mfma_probe(blocks: int = 2048, iters: int = 2000, out=None):
     return flop, out
 
 
-def hbm_probe(src, dst):
-    """Enqueue the HBM bandwidth probe: copy src into dst (same byte size,
-    contiguous device tensors)."""
-    nbytes = src.numel() * src.element_size()
-    if dst.numel() * dst.element_size() != nbytes or not (src.is_contiguous() and dst.is_contiguous()):
-        raise ValueError("src and dst must be contiguous and of the same byte size")
-    _call("fa_hbm_probe", _ptr(src), _ptr(dst), nbytes, _stream())
-    return dst
+HBM_PROBE_THREADS = 4096 * 256
+
+
+def hbm_probe(src, sink=None):
+    """Enqueue the HBM read probe over the bytes of src (a contiguous device
+    tensor whose size is a multiple of 16 bytes).  Returns the sink tensor
+    (one folded int32 per probe thread)."""
+    torch = _torch()
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    sink = torch.empty(HBM_PROBE_THREADS, dtype=torch.int32, device=src.device) if sink is None else sink
+    if sink.numel() < HBM_PROBE_THREADS or sink.element_size() != 4:
+        raise ValueError(f"sink must hold {HBM_PROBE_THREADS} 32-bit values")
+    _call("fa_hbm_probe", _ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream())
+    return sink
 
 
 # ---------------------------------------------------------------- autograd

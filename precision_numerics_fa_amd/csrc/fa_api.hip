@@ -283,15 +283,12 @@ long long fa_mfma_probe(float* out, int blocks, int iters, void* stream) {
   return ls != FA_OK ? ls : fa::mfma_probe_flop(blocks, iters);
 }
 
-int fa_hbm_probe(const void* src, void* dst, size_t bytes, void* stream) {
-  if (!aligned(src, 16) || !aligned(dst, 16) || bytes == 0 || bytes % 16 != 0) return FA_ERR_INVALID_ARG;
-  const char* a = static_cast<const char*>(src);
-  const char* b = static_cast<const char*>(dst);
-  if (a < b + bytes && b < a + bytes) return FA_ERR_INVALID_ARG;  // overlapping buffers
+int fa_hbm_probe(const void* src, size_t bytes, unsigned int* sink, void* stream) {
+  if (!aligned(src, 16) || !aligned(sink, 4) || bytes == 0 || bytes % 16 != 0) return FA_ERR_INVALID_ARG;
   const int st = check_device();
   if (st != FA_OK) return st;
   (void)hipGetLastError();
-  return launched(fa::launch_copy_probe(src, dst, (long long)(bytes / 16), static_cast<hipStream_t>(stream)));
+  return launched(fa::launch_read_probe(src, sink, (long long)(bytes / 16), static_cast<hipStream_t>(stream)));
 }
 
 const char* fa_status_string(int status) {

@@ -81,8 +81,10 @@ hipError_t launch_base_pv(const BaseArgs& a, hipStream_t stream);
 // `blocks` workgroups of `iters` iterations, and the launch.
 long long mfma_probe_flop(int blocks, int iters);
 hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t stream);
-// The HBM bandwidth probe: copies n16 16-byte units from src to dst.
-hipError_t launch_copy_probe(const void* src, void* dst, long long n16, hipStream_t stream);
+// The HBM read-bandwidth probe: reads n16 16-byte units of src; one folded
+// value per thread goes to sink (kHbmProbeBlocks * 256 of them).
+constexpr int kHbmProbeBlocks = 4096;
+hipError_t launch_read_probe(const void* src, uint32_t* sink, long long n16, hipStream_t stream);
 
 constexpr int kFwdBlockQ = 128;
 constexpr int kFwdBlockK = 64;

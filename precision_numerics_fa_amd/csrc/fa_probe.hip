@@ -5,8 +5,9 @@
 // peak.  Each wave keeps eight independent accumulator chains in flight, two
 // waves per SIMD; operands stay in registers, so neither memory nor LDS takes
 // part.  The result is written out so that the chains are not removed.
-// A second probe streams a buffer through HBM (16-byte loads and stores,
-// four independent loads in flight per lane) for the bandwidth ceiling.
+// A second probe reads a buffer through HBM (16-byte loads, four in flight
+// per lane) for the read-bandwidth ceiling of the memory-bound kernels, whose
+// traffic is almost all reads.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -36,26 +37,29 @@ __global__ __launch_bounds__(256, 2) void mfma_probe_kernel(float* __restrict__ 
   out[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
-// dst[i] = src[i] for i < n16 (16-byte units), grid-stride, four loads per
-// lane issued before their stores.
-__global__ __launch_bounds__(256) void copy_probe_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+// Streams src[0 .. n16) (16-byte units) through the lanes, four loads in
+// flight per lane, and folds each lane's words into one value (written to
+// sink[thread]) so that the loads are kept.
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ src, uint32_t* __restrict__ sink,
                                                          long long n16) {
   const long long stride = (long long)gridDim.x * 256;
   long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  uint32_t acc = 0;
   for (; i + 3 * stride < n16; i += 4 * stride) {
     const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    dst[i] = a;
-    dst[i + stride] = b;
-    dst[i + 2 * stride] = c;
-    dst[i + 3 * stride] = d;
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
   }
-  for (; i < n16; i += stride) dst[i] = src[i];
+  for (; i < n16; i += stride) {
+    const uint4 a = src[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  sink[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
 }  // namespace
 
-hipError_t launch_copy_probe(const void* src, void* dst, long long n16, hipStream_t s) {
-  hipLaunchKernelGGL(copy_probe_kernel, dim3(4096), dim3(256), 0, s, (const uint4*)src, (uint4*)dst, n16);
+hipError_t launch_read_probe(const void* src, uint32_t* sink, long long n16, hipStream_t s) {
+  hipLaunchKernelGGL(read_probe_kernel, dim3(kHbmProbeBlocks), dim3(256), 0, s, (const uint4*)src, sink, n16);
   return hipGetLastError();
 }
 

@@ -157,10 +157,10 @@ def test_probe_argument_validation(lib):
     assert lib.fa_mfma_probe(None, 8, 3, None) == -1
     assert lib.fa_mfma_probe(GOOD, 0, 3, None) == -1
     assert lib.fa_mfma_probe(GOOD, 8, 0, None) == -1
-    assert lib.fa_hbm_probe(GOOD, P(1 << 20), 100, None) == -1         # not a multiple of 16
-    assert lib.fa_hbm_probe(GOOD, P(4096 + 64), 256, None) == -1       # overlapping
-    assert lib.fa_hbm_probe(P(4100), P(1 << 20), 256, None) == -1      # misaligned
+    assert lib.fa_hbm_probe(GOOD, 100, P(1 << 20), None) == -1         # not a multiple of 16
+    assert lib.fa_hbm_probe(GOOD, 256, None, None) == -1               # no sink
+    assert lib.fa_hbm_probe(P(4100), 256, P(1 << 20), None) == -1      # misaligned
     import torch
     if not torch.cuda.is_available():
         assert lib.fa_mfma_probe(GOOD, 8, 3, None) == -5
-        assert lib.fa_hbm_probe(GOOD, P(1 << 20), 256, None) == -5
+        assert lib.fa_hbm_probe(GOOD, 256, P(1 << 20), None) == -5

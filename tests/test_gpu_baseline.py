@@ -223,15 +223,15 @@ def test_mfma_probe_counts_its_flop_and_computes_the_product(fa):
     assert np.array_equal(got, np.broadcast_to(expect, got.shape))
 
 
-def test_hbm_probe_copies(fa):
+def test_hbm_probe_reads_every_word(fa):
+    """The read probe folds (xor) each thread's words: the xor over all sink
+    values equals the xor of the whole buffer, including a tail shorter than
+    the grid stride."""
     import torch
-    src = torch.arange(1 << 20, dtype=torch.float32, device="cuda") * 0.5 + 3.0
-    dst = torch.zeros_like(src)
-    fa.hbm_probe(src, dst)
-    torch.cuda.synchronize()
-    assert torch.equal(src, dst)
-    src2 = torch.arange(12, dtype=torch.float32, device="cuda")   # 48 bytes: a tail shorter than the stride
-    dst2 = torch.zeros_like(src2)
-    fa.hbm_probe(src2, dst2)
-    torch.cuda.synchronize()
-    assert torch.equal(src2, dst2)
+    for n in (1 << 20, 12, 4096 * 256 * 4 * 3 + 40):
+        src = torch.randint(-2 ** 31, 2 ** 31 - 1, (n,), dtype=torch.int32, device="cuda")
+        sink = fa.hbm_probe(src)
+        torch.cuda.synchronize()
+        want = np.bitwise_xor.reduce(src.cpu().numpy().view(np.uint32))
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == want, n
