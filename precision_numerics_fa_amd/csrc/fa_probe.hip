@@ -37,19 +37,22 @@ __global__ __launch_bounds__(256, 2) void mfma_probe_kernel(float* __restrict__ 
   out[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
-// Streams src[0 .. n16) (16-byte units) through the lanes, four loads in
-// flight per lane, and folds each lane's words into one value (written to
-// sink[thread]) so that the loads are kept.
+// Reads src[0 .. n16) (16-byte units): each workgroup streams one
+// contiguous slice, 16 KB per step (four 16-byte loads in flight per lane),
+// and each lane folds its words into one value (written to sink[thread]) so
+// that the loads are kept.
 __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ src, uint32_t* __restrict__ sink,
                                                          long long n16) {
-  const long long stride = (long long)gridDim.x * 256;
-  long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long chunk = (n16 + gridDim.x - 1) / gridDim.x;
+  const long long begin = (long long)blockIdx.x * chunk;
+  const long long end = min(n16, begin + chunk);
+  long long i = begin + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+  for (; i + 768 < end; i += 1024) {
+    const uint4 a = src[i], b = src[i + 256], c = src[i + 512], d = src[i + 768];
     acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
   }
-  for (; i < n16; i += stride) {
+  for (; i < end; i += 256) {
     const uint4 a = src[i];
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
