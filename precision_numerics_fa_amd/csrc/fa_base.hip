@@ -34,7 +34,6 @@ namespace {
 
 constexpr int kBaseBQ = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int kBaseBK = 64;   // keys per block
-constexpr int kBaseSoftmaxChunks = kBaseMaxN / (4 * 256);  // float4 chunks per thread
 
 // Workgroup -> (head, query block), heaviest causal block first in each head.
 __device__ __forceinline__ void base_block(int n_qblk, int& bh, int& qb) {
@@ -133,70 +132,91 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// One workgroup per row: the row's visible scores (at most kBaseMaxN) are
-// read once into registers, 4 per chunk; the maximum and the sum are reduced
-// within each wave and then over the four waves in a fixed order, so the
-// result does not depend on timing.
-template <bool CAUSAL>
+// Row softmax.  A team of WPR waves owns a row: one wave per row (four rows
+// per workgroup) when rows are at most kBaseWaveRow keys, else the whole
+// workgroup.  The row's visible scores are read once into registers, 4 per
+// chunk; chunks past the row's end are skipped by team-uniform branches.  The
+// maximum and the sum are reduced within each wave and, for a workgroup team,
+// over its four waves in a fixed order, so the result does not depend on
+// timing.
+constexpr int kBaseWaveRow = 4096;
+
+template <bool CAUSAL, int WPR>
 __global__ __launch_bounds__(256) void base_softmax_kernel(const float* __restrict__ S, bf16_t* __restrict__ P,
-                                                           float* __restrict__ LSE, int N, int ld) {
+                                                           float* __restrict__ LSE, int N, int ld, long long rows) {
+  constexpr int TEAM = 64 * WPR;                     // threads per row
+  constexpr int CH = (WPR == 1 ? kBaseWaveRow : kBaseMaxN) / (4 * TEAM);  // float4 chunks per thread
   __shared__ float red[2][4];
-  const long long row = blockIdx.x;  // (b*H + h) * N + i
-  const int i = (int)(row % N);
   const int tid = threadIdx.x, wave = tid >> 6;
+  const long long row = WPR == 1 ? (long long)blockIdx.x * 4 + wave : (long long)blockIdx.x;  // (b*H + h)*N + i
+  if (WPR == 1 && row >= rows) return;              // a whole wave; this variant has no barrier
+  const int t = WPR == 1 ? (tid & 63) : tid;
+  const int i = (int)(row % N);
   const int L = CAUSAL ? i + 1 : N;                                            // visible keys
   const int W = CAUSAL ? min(ld, kBaseBK * (i / kBaseBK + 1)) : ld;           // keys the PV kernel reads
   const float* Srow = S + row * ld;
   bf16_t* Prow = P + row * ld;
 
-  float4 x[kBaseSoftmaxChunks];
+  float4 x[CH];
   float mx = kNegInf;
 #pragma unroll
-  for (int u = 0; u < kBaseSoftmaxChunks; ++u) {
-    const int j = 4 * (tid + 256 * u);
+  for (int u = 0; u < CH; ++u) {
     x[u] = make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
-    if (j < L) {
-      x[u] = *reinterpret_cast<const float4*>(Srow + j);
-      if (j + 1 >= L) x[u].y = kNegInf;
-      if (j + 2 >= L) x[u].z = kNegInf;
-      if (j + 3 >= L) x[u].w = kNegInf;
+    if (4 * TEAM * u < L) {
+      const int j = 4 * (t + TEAM * u);
+      if (j < L) {
+        x[u] = *reinterpret_cast<const float4*>(Srow + j);
+        if (j + 1 >= L) x[u].y = kNegInf;
+        if (j + 2 >= L) x[u].z = kNegInf;
+        if (j + 3 >= L) x[u].w = kNegInf;
+      }
+      mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fmaxf(x[u].x, x[u].y), __builtin_fmaxf(x[u].z, x[u].w)));
     }
-    mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fmaxf(x[u].x, x[u].y), __builtin_fmaxf(x[u].z, x[u].w)));
   }
   mx = wave_max(mx);
-  if ((tid & 63) == 0) red[0][wave] = mx;
-  __syncthreads();
-  const float r = __builtin_fmaxf(__builtin_fmaxf(red[0][0], red[0][1]), __builtin_fmaxf(red[0][2], red[0][3]));
+  float r = mx;
+  if (WPR == 4) {
+    if ((tid & 63) == 0) red[0][wave] = mx;
+    __syncthreads();
+    r = __builtin_fmaxf(__builtin_fmaxf(red[0][0], red[0][1]), __builtin_fmaxf(red[0][2], red[0][3]));
+  }
 
   float sum = 0.0f;
 #pragma unroll
-  for (int u = 0; u < kBaseSoftmaxChunks; ++u) {
-    x[u].x = exp2_fast((x[u].x - r) * kLog2e);  // masked: exp2(-inf) = 0
-    x[u].y = exp2_fast((x[u].y - r) * kLog2e);
-    x[u].z = exp2_fast((x[u].z - r) * kLog2e);
-    x[u].w = exp2_fast((x[u].w - r) * kLog2e);
-    sum += x[u].x;
-    sum += x[u].y;
-    sum += x[u].z;
-    sum += x[u].w;
+  for (int u = 0; u < CH; ++u) {
+    if (4 * TEAM * u < L) {
+      x[u].x = exp2_fast((x[u].x - r) * kLog2e);  // masked: exp2(-inf) = 0
+      x[u].y = exp2_fast((x[u].y - r) * kLog2e);
+      x[u].z = exp2_fast((x[u].z - r) * kLog2e);
+      x[u].w = exp2_fast((x[u].w - r) * kLog2e);
+      sum += x[u].x;
+      sum += x[u].y;
+      sum += x[u].z;
+      sum += x[u].w;
+    } else {
+      x[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
   }
   sum = wave_sum(sum);
-  if ((tid & 63) == 0) red[1][wave] = sum;
-  __syncthreads();
-  const float l = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
+  float l = sum;
+  if (WPR == 4) {
+    if ((tid & 63) == 0) red[1][wave] = sum;
+    __syncthreads();
+    l = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
+  }
   const float inv = 1.0f / l;
 
 #pragma unroll
-  for (int u = 0; u < kBaseSoftmaxChunks; ++u) {
-    const int j = 4 * (tid + 256 * u);
-    if (j < W) {
+  for (int u = 0; u < CH; ++u) {
+    const int j = 4 * (t + TEAM * u);
+    if (4 * TEAM * u < W && j < W) {
       uint2 w;
       w.x = pack2<__bf16>(x[u].x * inv, x[u].y * inv);
       w.y = pack2<__bf16>(x[u].z * inv, x[u].w * inv);
       *reinterpret_cast<uint2*>(Prow + j) = w;
     }
   }
-  if (tid == 0) LSE[row] = r + __builtin_log2f(l) * kLn2;
+  if (t == 0) LSE[row] = r + __builtin_log2f(l) * kLn2;
 }
 
 // ---------------------------------------------------------------- O = P V
@@ -329,13 +349,24 @@ hipError_t launch_base_scores(const BaseArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_base_softmax(const BaseArgs& a, hipStream_t s) {
-  const unsigned grid = (unsigned)((long long)a.B * a.H * a.N);
-  if (a.causal)
-    hipLaunchKernelGGL((base_softmax_kernel<true>), dim3(grid), dim3(256), 0, s, a.s, (bf16_t*)a.p, a.lse, a.N,
-                       a.ld);
-  else
-    hipLaunchKernelGGL((base_softmax_kernel<false>), dim3(grid), dim3(256), 0, s, a.s, (bf16_t*)a.p, a.lse, a.N,
-                       a.ld);
+  const long long rows = (long long)a.B * a.H * a.N;
+  if (a.ld <= kBaseWaveRow) {
+    const unsigned grid = (unsigned)((rows + 3) / 4);
+    if (a.causal)
+      hipLaunchKernelGGL((base_softmax_kernel<true, 1>), dim3(grid), dim3(256), 0, s, a.s, (bf16_t*)a.p, a.lse, a.N,
+                         a.ld, rows);
+    else
+      hipLaunchKernelGGL((base_softmax_kernel<false, 1>), dim3(grid), dim3(256), 0, s, a.s, (bf16_t*)a.p, a.lse,
+                         a.N, a.ld, rows);
+  } else {
+    const unsigned grid = (unsigned)rows;
+    if (a.causal)
+      hipLaunchKernelGGL((base_softmax_kernel<true, 4>), dim3(grid), dim3(256), 0, s, a.s, (bf16_t*)a.p, a.lse, a.N,
+                         a.ld, rows);
+    else
+      hipLaunchKernelGGL((base_softmax_kernel<false, 4>), dim3(grid), dim3(256), 0, s, a.s, (bf16_t*)a.p, a.lse,
+                         a.N, a.ld, rows);
+  }
   return hipGetLastError();
 }
 

@@ -235,3 +235,29 @@ def test_hbm_probe_reads_every_word(fa):
         want = np.bitwise_xor.reduce(src.cpu().numpy().view(np.uint32))
         got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
         assert got == want, n
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_baseline_at_its_longest_rows(fa, causal):
+    """N = 16384, the longest row the baseline's softmax holds in registers
+    (one head of each head size): sampled rows against the exact oracle row
+    by row, and the last rows of the tail."""
+    import torch
+    N = 16384
+    for d in (64, 128):
+        say(f"base longest rows N={N} d={d} causal={causal}")
+        bits, dev = random_case(1, 1, N, d, seed=91 + d + int(causal))
+        scale = 1.0 / np.sqrt(d)
+        o, lse = fa.base_fwd(dev["q"], dev["k"], dev["v"], causal=causal)
+        torch.cuda.synchronize()
+        q, k, v = (head_f64(bits[n])[0, 0] for n in ("q", "k", "v"))
+        rows = np.concatenate([np.random.default_rng(d).choice(N, 24, replace=False), [0, 63, 64, N - 2, N - 1]])
+        og, lg = to_f64(o)[0, 0], to_f64(lse)[0, 0]
+        for i in rows:
+            L = i + 1 if causal else N
+            s = scale * (k[:L] @ q[i])
+            r = s.max()
+            e = np.exp(s - r)
+            o_ref = (e / e.sum()) @ v[:L]
+            assert np.abs(og[i] - o_ref).max() <= 1.5e-2, i
+            assert abs(lg[i] - (r + np.log(e.sum()))) <= 1e-4, i
