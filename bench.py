@@ -263,10 +263,53 @@ def main():
     base = baseline_leg(args, q, k, v, fwd_flop, kern_ms["fwd"])
     out["baseline_fp32acc"] = base.pop("record")
     if not args.no_cpu_baseline:
+        out["tie_bias"] = tie_bias_leg()
         out.update(cpu_baseline_leg(w, full, o, lse, dq, dk, dv, args.cpu_heads, fwd_flop + bwd_flop,
                                     compare={"flash_fix_on": o, "flash_fix_off": o_plain,
                                              "baseline_fp32acc": base["o"]}))
     print(json.dumps(out), flush=True)
+
+
+def tie_bias_leg(batches=(0, 1, 2, 3)):
+    """The mean signed error on rows whose maximum repeats, with the fix off
+    and on: the tie-heavy workload (8, 12, 1024, 64, causal, Q and K x 4, 5%
+    of rows given a repeated maximum), FlashAttention on the GPU against the
+    float64 oracle on the heads of the given batch entries.  "aligned" signs
+    each error by the side of the tied values' mean the exact output lies on
+    (the direction of the bias); non-tie rows are the control."""
+    import numpy as np
+    import torch
+
+    import fa_inputs as F
+    import precision_numerics_fa_amd as fa
+    from oracle import metrics as Mt
+    from oracle import reference as REF
+
+    w = F.WORKLOADS["c2"]
+    full = F.full(w)
+    q, k, v = (torch.from_numpy(full[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v"))
+    outs = {flag: fa.fwd(q, k, v, causal=True, stabilize=flag)[0].float().cpu().numpy() for flag in (False, True)}
+    rec = {"workload": f"{w.B}x{w.H}x{w.N}x{w.d} causal, Q and K x 4, 5% repeated-maximum rows",
+           "heads": len(batches) * w.H}
+    diffs = {False: [], True: []}
+    refs, metas = [], []
+    for b in batches:
+        qh, kh, vh = (F.bf16_bits_to_f32(full[n][b]).astype(np.float64) for n in ("q", "k", "v"))
+        o_ref, _ = REF.forward(qh, kh, vh, w.scale, True)
+        refs.append(o_ref)
+        metas.append(REF.tie_metadata(qh, kh, vh, w.scale, True))
+    o_ref = np.stack(refs)
+    count = np.stack([m["count"] for m in metas])
+    tmean = np.stack([m["tie_mean"] for m in metas])
+    for flag in (False, True):
+        o = outs[flag][list(batches)]
+        rep = Mt.tie_report(o, o_ref, count, tmean)
+        rec["fix_on" if flag else "fix_off"] = {
+            part: {key: (round(val, 9) if isinstance(val, float) else val) for key, val in stats.items()}
+            for part, stats in rep.items()}
+    del q, k, v
+    torch.cuda.empty_cache()
+    return rec
 
 
 def measured_peaks():
