@@ -35,10 +35,34 @@ namespace {
 constexpr int kBaseBQ = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int kBaseBK = 64;   // keys per block
 
-// Workgroup -> (head, query block), heaviest causal block first in each head.
-__device__ __forceinline__ void base_block(int n_qblk, int& bh, int& qb) {
-  bh = blockIdx.x / n_qblk;
-  qb = n_qblk - 1 - (int)(blockIdx.x - bh * n_qblk);
+// Workgroup -> (head, query block).  The hardware hands workgroup i to XCD
+// i % 8; with `remap` each XCD gets a contiguous group of G heads, walked
+// head-major with the heaviest causal block first, so that a head's K (or V)
+// stays in that XCD's L2 while the N x N matrix streams past it.  Returns
+// false for the padding workgroups of the last group.
+__device__ __forceinline__ bool base_block(int n_qblk, int total, int remap, int BH, int G, int& bh, int& qb) {
+  int bid = blockIdx.x;
+  if (remap) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+  const int per_group = G * n_qblk;
+  const int g = bid / per_group;
+  const int r = bid - g * per_group;
+  bh = g * G + r / n_qblk;
+  qb = n_qblk - 1 - r % n_qblk;
+  return bh < BH;
+}
+
+struct BaseGrid {
+  int n_qblk, total, remap, BH, G;
+};
+
+BaseGrid base_grid(const BaseArgs& a) {
+  BaseGrid g;
+  g.n_qblk = (a.N + kBaseBQ - 1) / kBaseBQ;
+  g.BH = a.B * a.H;
+  g.G = (g.BH + 7) / 8;
+  g.total = (g.BH + g.G - 1) / g.G * g.G * g.n_qblk;
+  g.remap = g.total % 8 == 0 ? 1 : 0;
+  return g;
 }
 
 // ---------------------------------------------------------------- S = scale * Q K^T
@@ -48,12 +72,12 @@ __device__ __forceinline__ void base_block(int n_qblk, int& bh, int& qb) {
 // instruction writes two 128-byte row segments.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void base_scores_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
-                                                          float* __restrict__ S, int N, int ld, int n_qblk,
+                                                          float* __restrict__ S, int N, int ld, BaseGrid grid,
                                                           float scale) {
   constexpr int TILE = kBaseBK * D;
   __shared__ __attribute__((aligned(16))) bf16_t smem[2 * TILE];
   int bh, qb;
-  base_block(n_qblk, bh, qb);
+  if (!base_block(grid.n_qblk, grid.total, grid.remap, grid.BH, grid.G, bh, qb)) return;
   const int q0 = qb * kBaseBQ;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -225,12 +249,12 @@ __global__ __launch_bounds__(256) void base_softmax_kernel(const float* __restri
 // straight from HBM as the B operand, O^T accumulated in FP32 registers.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void base_pv_kernel(const bf16_t* __restrict__ P, const bf16_t* __restrict__ V,
-                                                      bf16_t* __restrict__ O, int N, int ld, int n_qblk) {
+                                                      bf16_t* __restrict__ O, int N, int ld, BaseGrid grid) {
   constexpr int TILE = kBaseBK * D;
   constexpr int NK = kBaseBK / 16;
   __shared__ __attribute__((aligned(16))) bf16_t smem[2 * TILE];
   int bh, qb;
-  base_block(n_qblk, bh, qb);
+  if (!base_block(grid.n_qblk, grid.total, grid.remap, grid.BH, grid.G, bh, qb)) return;
   const int q0 = qb * kBaseBQ;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -316,27 +340,25 @@ __global__ __launch_bounds__(256) void base_pv_kernel(const bf16_t* __restrict__
 
 template <int D>
 hipError_t scores_d(const BaseArgs& a, hipStream_t s) {
-  const int n_qblk = (a.N + kBaseBQ - 1) / kBaseBQ;
-  const unsigned grid = (unsigned)((long long)a.B * a.H * n_qblk);
+  const BaseGrid g = base_grid(a);
   if (a.causal)
-    hipLaunchKernelGGL((base_scores_kernel<D, true>), dim3(grid), dim3(256), 0, s, (const bf16_t*)a.q,
-                       (const bf16_t*)a.k, a.s, a.N, a.ld, n_qblk, a.scale);
+    hipLaunchKernelGGL((base_scores_kernel<D, true>), dim3((unsigned)g.total), dim3(256), 0, s, (const bf16_t*)a.q,
+                       (const bf16_t*)a.k, a.s, a.N, a.ld, g, a.scale);
   else
-    hipLaunchKernelGGL((base_scores_kernel<D, false>), dim3(grid), dim3(256), 0, s, (const bf16_t*)a.q,
-                       (const bf16_t*)a.k, a.s, a.N, a.ld, n_qblk, a.scale);
+    hipLaunchKernelGGL((base_scores_kernel<D, false>), dim3((unsigned)g.total), dim3(256), 0, s, (const bf16_t*)a.q,
+                       (const bf16_t*)a.k, a.s, a.N, a.ld, g, a.scale);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t pv_d(const BaseArgs& a, hipStream_t s) {
-  const int n_qblk = (a.N + kBaseBQ - 1) / kBaseBQ;
-  const unsigned grid = (unsigned)((long long)a.B * a.H * n_qblk);
+  const BaseGrid g = base_grid(a);
   if (a.causal)
-    hipLaunchKernelGGL((base_pv_kernel<D, true>), dim3(grid), dim3(256), 0, s, (const bf16_t*)a.p,
-                       (const bf16_t*)a.v, (bf16_t*)a.o, a.N, a.ld, n_qblk);
+    hipLaunchKernelGGL((base_pv_kernel<D, true>), dim3((unsigned)g.total), dim3(256), 0, s, (const bf16_t*)a.p,
+                       (const bf16_t*)a.v, (bf16_t*)a.o, a.N, a.ld, g);
   else
-    hipLaunchKernelGGL((base_pv_kernel<D, false>), dim3(grid), dim3(256), 0, s, (const bf16_t*)a.p,
-                       (const bf16_t*)a.v, (bf16_t*)a.o, a.N, a.ld, n_qblk);
+    hipLaunchKernelGGL((base_pv_kernel<D, false>), dim3((unsigned)g.total), dim3(256), 0, s, (const bf16_t*)a.p,
+                       (const bf16_t*)a.v, (bf16_t*)a.o, a.N, a.ld, g);
   return hipGetLastError();
 }
 
