@@ -36,6 +36,7 @@ PEAK_BF16_TFLOPS = 2500.0       # MI355X dense BF16 MFMA
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 METRIC = "attn fwd/bwd TFLOP/s & % BF16 MFMA peak (1 GPU); max/mean |err| vs FP64 oracle"
 KERNEL_SOURCES = ["fa_device.hpp", "fa_fwd.hip", "fa_bwd.hip"]
+BASE_KERNEL_SOURCES = ["fa_device.hpp", "fa_base.hip"]
 
 
 def parse():
@@ -69,11 +70,11 @@ def copy_probe(mib: int) -> None:
     print(json.dumps({"copy_probe_bytes": n * 4, "launches": 5}), flush=True)
 
 
-def source_digest() -> str:
+def source_digest(sources=None) -> str:
     """Digest of the kernel sources with comments and blank space removed, so
     that the stored counter figures stay valid across comment-only edits."""
     h = hashlib.sha256()
-    for s in KERNEL_SOURCES:
+    for s in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, "precision_numerics_fa_amd", "csrc", s)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -84,13 +85,18 @@ def source_digest() -> str:
 
 def _counter_record(name: str, kernel: str):
     """Per-kernel record of a committed rocprofv3 counter summary, if it was
-    taken on the current kernel sources; else None."""
+    taken on the current kernel sources; else None.  The baseline's kernels
+    carry the digest of their own sources."""
     path = os.path.join(ROOT, "profiles", name)
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
+    if kernel.startswith("base_"):
+        if rec.get("base_source_digest") != source_digest(BASE_KERNEL_SOURCES):
+            return None
+        return rec.get("base_kernels", {}).get(kernel)
     if rec.get("source_digest") != source_digest():
         return None
     return rec.get("kernels", {}).get(kernel)
@@ -379,7 +385,7 @@ def baseline_leg(args, q, k, v, fwd_flop, fa_fwd_ms):
         ach = algo[n] / (ms[n] * 1e-3) / 1e9
         kernels[n] = {"kernel": names[n], "ms": round(ms[n], 4), "bound": "hbm", "achieved": round(ach, 1),
                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                      "bytes": algo[n]}
+                      "bytes": algo[n], "traffic": counter_traffic(names[n])}
     total = sum(ms.values())
     # the same call through the one-shot entry point, bitwise the steps' result
     ob2, _ = fa.base_fwd(q, k, v, causal=True)
