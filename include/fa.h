@@ -42,7 +42,11 @@
  *     no state between calls; calls are thread-safe.
  *   - Arguments are validated before any launch; on an error return nothing
  *     has been enqueued and no output has been written.  Non-finite input
- *     values are not checked; they propagate to the rows they touch.
+ *     values are not checked; they propagate to the rows they touch: a
+ *     non-finite Q row to that output row, a non-finite K row to the rows that
+ *     see that key, and a non-finite V row to every row that processes the
+ *     64-key block holding it (the masked keys of a block still enter its
+ *     product with V, with probability 0).
  */
 #ifndef FA_H
 #define FA_H

@@ -378,3 +378,27 @@ def test_autograd_attention_matches_the_abi_calls(fa, dtype):
     assert torch.equal(o.detach(), o2)
     for t, g in zip((q, k, v), g2):
         assert torch.equal(t.grad, g)
+
+
+@pytest.mark.parametrize("stabilize", [False, True])
+def test_nonfinite_q_and_k_stay_in_their_rows(fa, stabilize):
+    """Non-finite inputs are not checked; a NaN in a query row reaches only that
+    row, and a NaN in a key row only the (causal) rows that see that key: every
+    other output row is bitwise the clean run's, in that head and the others."""
+    import torch
+    say(f"nonfinite stabilize={stabilize}")
+    B, H, N, d = 1, 2, 200, 64
+    bits, dev = random_case(B, H, N, d, seed=4242)
+    o0, l0 = fa.fwd(dev["q"], dev["k"], dev["v"], causal=True, stabilize=stabilize)
+    q, k = dev["q"].clone(), dev["k"].clone()
+    q[0, 0, 37, 5] = float("nan")
+    k[0, 0, 150, 3] = float("nan")
+    o1, l1 = fa.fwd(q, k, dev["v"], causal=True, stabilize=stabilize)
+    o0, o1, l0, l1 = (t.float().cpu().numpy() for t in (o0, o1, l0, l1))
+    assert np.array_equal(o1[0, 1], o0[0, 1]) and np.array_equal(l1[0, 1], l0[0, 1])
+    clean = np.ones(N, dtype=bool)
+    clean[37] = False
+    clean[150:] = False
+    assert np.array_equal(o1[0, 0][clean], o0[0, 0][clean])
+    assert np.array_equal(l1[0, 0][clean], l0[0, 0][clean])
+    assert np.isnan(o1[0, 0][~clean]).all() and np.isnan(l1[0, 0][~clean]).all()
