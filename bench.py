@@ -551,6 +551,14 @@ def cpu_baseline_leg(w, full, o, lse, dq, dk, dv, heads, step_flop, compare=None
     per_head_flop = step_flop / (w.B * w.H)
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     cpu_tflops = per_head_flop * len(pairs) / t_cpu / 1e12
+    cpu_model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            names = [ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")]
+        if names:
+            cpu_model = names[0]
+    except OSError:
+        pass
     for dv_ in dev_stats.values():
         dv_["mean_abs"] = float(np.mean(dv_["mean_abs"]))
     # oracle B (the bf16 blocked emulation of the forward) on one of the heads
@@ -575,7 +583,9 @@ def cpu_baseline_leg(w, full, o, lse, dq, dk, dv, heads, step_flop, compare=None
                          "sample": f"float64 oracle forward+backward on {len(pairs)} of {w.B * w.H} heads "
                                    f"(N={w.N}, d={w.d}, causal), {t_cpu:.1f} s; TFLOP/s under the "
                                    f"GPU's algorithmic FLOP count",
-                         "cpu": platform.processor() or platform.machine(), "seconds": round(t_cpu, 2),
+                         "cpu": cpu_model, "host_cpus": os.cpu_count(), "seconds": round(t_cpu, 2),
+                         "seconds_per_head": round(t_cpu / len(pairs), 3),
+                         "extrapolated_full_s": round(t_cpu / len(pairs) * w.B * w.H, 1),
                          "oracle_b_forward_s_per_head": round(t_emu, 2)},
         "accuracy": {"heads_checked": len(pairs), "o_max_abs": errs["max_abs"], "o_mean_abs": errs["mean_abs"],
                      "o_max_rel_normwise": errs["max_rel_normwise"], "lse_max_abs": errs["lse_max_abs"],
