@@ -164,3 +164,35 @@ def test_probe_argument_validation(lib):
     if not torch.cuda.is_available():
         assert lib.fa_mfma_probe(GOOD, 8, 3, None) == -5
         assert lib.fa_hbm_probe(GOOD, 256, P(1 << 20), None) == -5
+
+
+def test_header_is_plain_c_and_links(lib, tmp_path):
+    """include/fa.h is a C header: a C99 program that takes the address of
+    every declared entry point compiles with gcc and links against libfa.so,
+    and a forward call made from C with an invalid size returns
+    FA_ERR_INVALID_ARG (checked before any device work, so the call never
+    reaches a GPU)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    names = _declared()
+    src = tmp_path / "abi.c"
+    src.write_text(
+        "#include <stdio.h>\n#include \"fa.h\"\n"
+        "int main(void) {\n"
+        "  void* fns[] = {" + ", ".join(f"(void*){n}" for n in names) + "};\n"
+        "  int st = fa_fwd((void*)4096, (void*)4096, (void*)4096, (void*)4096, (float*)4096,\n"
+        "                  1, 1, 0, 64, 0, 0.125f, 0, 0);\n"
+        "  printf(\"%d %d %s\\n\", (int)(sizeof(fns) / sizeof(fns[0])), st, fa_status_string(st));\n"
+        "  return 0;\n}\n")
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(fa.lib_path())
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src),
+                    "-L", libdir, "-lfa", f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stderr
+    count, status = (int(x) for x in out.stdout.split()[:2])
+    assert count == len(names)
+    assert status == -1
