@@ -87,6 +87,29 @@ int fa_fwd_diag(const void* Q, const void* K, const void* V, void* O, float* LSE
                 int B, int H, int N, int d, int causal, float scale, int stabilize,
                 void* stream);
 
+/* Forward pass split over keys, for launches too small to fill the GPU (a
+ * single head, short sequences).  Each (head, 128-row query block) is cut
+ * into `splits` contiguous ranges of its 64-key blocks, one workgroup each.
+ * A workgroup first replays the key blocks before its range through the
+ * running row maximum and repeated-maximum bookkeeping alone (scores only,
+ * no exponentials or products), so its own blocks are shifted, and their
+ * unnormalised probabilities rounded to BF16, exactly as in one pass over
+ * the row (page 2, "Mechanism 2": the fix acts on the running maximum of a
+ * row).  It writes its unnormalised output, row sum and final shift M_s to
+ * the workspace; a second launch merges the ranges with weights
+ * 2^(M_s - M), M the last range's shift (the row's):
+ *   O = bf16(sum_s 2^(M_s - M) O_bar_s / sum_s 2^(M_s - M) l_s).
+ * Against fa_fwd only the FP32 rounding of those rescalings differs (one
+ * product per range instead of one per block); with splits = 1 the result
+ * is bitwise fa_fwd's.  bf16 tensors as in fa_fwd; 1 <= splits <= 64; the
+ * workspace (256-byte aligned) holds at least
+ * fa_fwd_split_workspace_bytes() bytes.  Two launches. */
+size_t fa_fwd_split_workspace_bytes(int B, int H, int N, int d, int splits);
+int fa_fwd_split(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                 int splits, void* workspace, size_t workspace_bytes,
+                 int B, int H, int N, int d, int causal, float scale, int stabilize,
+                 void* stream);
+
 /* Bytes of device workspace fa_bwd needs: the fp32 vector D = rowsum(dO*O)
  * of shape (B,H,N), rounded up to 256 bytes.  Returns 0 for invalid sizes. */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int causal);

@@ -40,6 +40,8 @@ from ._lib import (  # noqa: F401
     fwd,
     fwd_diag,
     fwd_ex,
+    fwd_split,
+    fwd_split_workspace_bytes,
     fwd_tile,
     lib_path,
     hbm_probe,

@@ -26,6 +26,8 @@ _SIGNATURES = {
     "fa_bwd_grads": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "fa_fwd_ex": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_ex": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_fwd_split_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "fa_fwd_split": (_I, [_P, _P, _P, _P, _P, _I, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_base_ld": (_I, [_I]),
     "fa_base_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "fa_base_fwd": (_I, [_P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _P]),
@@ -182,6 +184,32 @@ def fwd_diag(q, k, v, causal: bool = False, scale: Optional[float] = None, stabi
     _call("fa_fwd_diag", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), _ptr(flags), B, H, N, d,
           int(bool(causal)), _scale(scale, d), int(bool(stabilize)), _stream())
     return o, l, flags
+
+
+def fwd_split_workspace_bytes(B: int, H: int, N: int, d: int, splits: int) -> int:
+    return int(load().fa_fwd_split_workspace_bytes(B, H, N, d, int(splits)))
+
+
+def fwd_split(q, k, v, splits: int, causal: bool = False, scale: Optional[float] = None,
+              stabilize: bool = False, workspace=None, out=None, lse=None):
+    """Forward pass split over `splits` key ranges per query block (bf16).
+    Returns (O, LSE) as fwd does."""
+    torch = _torch()
+    B, H, N, d = _shape(q)
+    dev = q.device
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check(n, t, torch.bfloat16, (B, H, N, d), dev)
+    need = fwd_split_workspace_bytes(B, H, N, d, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _check("out", o, torch.bfloat16, (B, H, N, d), dev)
+    _check("lse", l, torch.float32, (B, H, N), dev)
+    _call("fa_fwd_split", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), int(splits), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), B, H, N, d, int(bool(causal)), _scale(scale, d),
+          int(bool(stabilize)), _stream())
+    return o, l
 
 
 def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,

@@ -117,6 +117,21 @@ fa::BaseArgs base_args(const void* Q, const void* K, const void* V, void* O, flo
   return fa::BaseArgs{Q, K, V, O, LSE, S, P, B, H, N, d, fa::base_ld(N), causal != 0, scale};
 }
 
+// Workspace of fa_fwd_split: O_bar (splits, B*H, N, d) fp32, then l and M
+// (splits, B*H, N) fp32 each, every part at a 256-byte boundary.
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t split_obar_bytes(int splits, int B, int H, int N, int d) {
+  return round256((size_t)splits * B * H * N * d * sizeof(float));
+}
+size_t split_vec_bytes(int splits, int B, int H, int N) { return round256((size_t)splits * B * H * N * sizeof(float)); }
+
+int check_splits(int splits, int B, int H, int N) {
+  if (splits < 1 || splits > fa::kMaxSplits) return FA_ERR_INVALID_ARG;
+  const long long n_qblk = (N + fa::kFwdBlockQ - 1) / fa::kFwdBlockQ;
+  if ((long double)B * H * n_qblk * splits >= 2147483647.0L) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -208,6 +223,33 @@ int fa_bwd_ex(int dtype, const void* Q, const void* K, const void* V, const void
               int N, int d, int causal, float scale, int stabilize, void* stream) {
   return bwd_impl(dtype, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, B, H, N, d, causal, scale,
                   stabilize, stream);
+}
+
+size_t fa_fwd_split_workspace_bytes(int B, int H, int N, int d, int splits) {
+  if (check_shape(B, H, N, d) != FA_OK || check_splits(splits, B, H, N) != FA_OK) return 0;
+  return split_obar_bytes(splits, B, H, N, d) + 2 * split_vec_bytes(splits, B, H, N);
+}
+
+int fa_fwd_split(const void* Q, const void* K, const void* V, void* O, float* LSE, int splits, void* workspace,
+                 size_t workspace_bytes, int B, int H, int N, int d, int causal, float scale, int stabilize,
+                 void* stream) {
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if ((st = check_splits(splits, B, H, N)) != FA_OK) return st;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 4))
+    return FA_ERR_INVALID_ARG;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (workspace == nullptr || !aligned(workspace, 256) ||
+      workspace_bytes < fa_fwd_split_workspace_bytes(B, H, N, d, splits))
+    return FA_ERR_WORKSPACE;
+  if ((st = check_device()) != FA_OK) return st;
+  char* w = static_cast<char*>(workspace);
+  const size_t ob = split_obar_bytes(splits, B, H, N, d), vb = split_vec_bytes(splits, B, H, N);
+  fa::SplitArgs sa{reinterpret_cast<float*>(w), reinterpret_cast<float*>(w + ob),
+                   reinterpret_cast<float*>(w + ob + vb), splits};
+  fa::FwdArgs a{Q, K, V, O, LSE, nullptr, B, H, N, d, causal != 0, stabilize != 0, scale, fa::kBF16};
+  (void)hipGetLastError();
+  return launched(fa::launch_fwd_split(a, sa, static_cast<hipStream_t>(stream)));
 }
 
 int fa_base_ld(int N) { return N < 1 ? 0 : fa::base_ld(N); }

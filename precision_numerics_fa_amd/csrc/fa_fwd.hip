@@ -56,11 +56,25 @@ struct RowState {
   bool ever;   // the shift was applied at some block
 };
 
-template <typename E, int D, bool CAUSAL, bool STAB, bool DIAG>
+// Split-key mode: the partial results of one key range (see fwd_kernel).
+struct SplitOut {
+  float* obar;  // (splits, B*H, N, d) unnormalised output, fp32
+  float* lrow;  // (splits, B*H, N) row sum
+  float* mrow;  // (splits, B*H, N) shift M at the end of the range (base-2 units)
+  int splits;
+};
+
+// SPLIT: the workgroup covers one of `splits` contiguous ranges of its key
+// blocks.  It first replays the blocks before its range through the row
+// maximum and repeated-maximum bookkeeping only (scores, no exponentials or
+// products), so that its own blocks see the same running state, and hence
+// the same shift and the same rounding of P, as in one pass; it then writes
+// its unnormalised output, row sum and final shift for the merge kernel.
+template <typename E, int D, bool CAUSAL, bool STAB, bool DIAG, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     bf16_t* __restrict__ O, float* __restrict__ LSE, uint8_t* __restrict__ row_shifted,
-    int N, int n_qblk, int total_blocks, int xcd_remap, float c2, int BH, int G, int block_major) {
+    int N, int n_qblk, int total_blocks, int xcd_remap, float c2, int BH, int G, int block_major, SplitOut sp) {
   using T = FwdTile<D>;
   constexpr int NS = T::BK / 32;   // 32-key subtiles per block
   constexpr int NK = T::BK / 16;   // 16-key MFMA steps per block
@@ -74,7 +88,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   // i % 8; the remap gives each XCD a contiguous range of the order below.
   // The heaviest (last, for causal) query blocks go first.
   int bid = blockIdx.x;
-  if (xcd_remap) bid = (bid & 7) * (total_blocks >> 3) + (bid >> 3);
+  int split = 0;
+  if (SPLIT) {  // workgroup -> (key range, then head and query block, block-major)
+    split = bid % sp.splits;
+    bid /= sp.splits;
+  } else if (xcd_remap) {
+    bid = (bid & 7) * (total_blocks >> 3) + (bid >> 3);
+  }
   // The heads are split into groups of G, one per XCD.  Within a group the
   // query blocks go head-major (a head's K/V stay in L2) or, for launches of
   // a few rounds of workgroups, block-major (every head's heaviest block
@@ -104,6 +124,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   const int n_kblk = CAUSAL ? (last_row / T::BK + 1) : (N + T::BK - 1) / T::BK;
   // key blocks this wave computes (its causal bound), 0 for a wave past N
   const int n_wave = !wave_live ? 0 : (CAUSAL ? min(n_kblk, wave_last_q / T::BK + 1) : n_kblk);
+  // key blocks [jb, je) of this workgroup (all of them unless SPLIT)
+  const int jb = SPLIT ? split * n_kblk / sp.splits : 0;
+  const int je = SPLIT ? (split + 1) * n_kblk / sp.splits : n_kblk;
 
   // Q rows of this wave as B operands: element j of step kk is d = 16 kk + 8 hi + j.
   bf16x8 qf[D / 16];
@@ -153,9 +176,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
       }
   };
 
-  // Online softmax of one block held in s (masked already): updates the row
-  // state, rescales O, and returns bf16(P) as B operands in pb.
-  auto softmax = [&](f32x16* s, bf16x8* pb) {
+  // Row maximum and repeated-maximum bookkeeping of one block held in s
+  // (masked already): updates m (and the tie state) and returns the new shift.
+  auto track = [&](const f32x16* s) {
     // block row maximum; stabilised: also the second largest value, two
     // entries at a time: a' = max(a, x, y), b' = max(b, med3(a, x, y))
     float mx = kNegInf, m2 = kNegInf;
@@ -189,9 +212,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
       Mn = row_offset<E>(R, st.tied);
       if (DIAG) st.ever = st.ever || st.tied;
     }
+    st.m = m_new;
+    return Mn;
+  };
+
+  // Online softmax of one block held in s (masked already): updates the row
+  // state, rescales O, and returns bf16(P) as B operands in pb.
+  auto softmax = [&](f32x16* s, bf16x8* pb) {
+    const float Mn = track(s);
     const float alpha = exp2_fast(st.M - Mn);  // 0 on the first block (M = -inf)
     st.M = Mn;
-    st.m = m_new;
     float lsum = 0.0f;
 #pragma unroll
     for (int t = 0; t < NS; ++t)
@@ -234,33 +264,55 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
       }
   };
 
-  // ---- prologue: K0, V0 (and K1) into LDS; scores of block 0
-  load_tile_async<D, T::BK, 256>(ldoff, Kh, 0, N, Kbuf, wave, lane);
-  load_tile_async<D, T::BK, 256>(ldoff, Vh, 0, N, Vbuf, wave, lane);
-  if (n_kblk > 1) load_tile_async<D, T::BK, 256>(ldoff, Kh, T::BK, N, Kbuf + T::TILE, wave, lane);
-  wait_vmem();
-  wait_vmem_tracked();
-  zero_tail<D, T::BK, 256>(0, N, Kbuf, wave, lane);
-  zero_tail<D, T::BK, 256>(0, N, Vbuf, wave, lane);
-  if (n_kblk > 1) zero_tail<D, T::BK, 256>(T::BK, N, Kbuf + T::TILE, wave, lane);
-  __syncthreads();
-
   // Two score buffers swap roles every block (the loop is unrolled by two),
   // so the next block's scores need no register copy.
   f32x16 sa[NS], sb[NS];
-  if (n_wave > 0) scores(Kbuf, sa);
-  // The first iteration copies block 2 into the tile these scores were just
-  // read from; every wave's reads of it must be complete before any wave
-  // issues that copy.
-  if (n_kblk > 2) __syncthreads();
+
+  if (SPLIT) {
+    // ---- replay of the blocks before this range: scores and the running
+    // maximum / repeated-maximum state only, one K tile at a time
+    wait_vmem_tracked();
+    for (int j = 0; j < jb; ++j) {
+      load_tile_async<D, T::BK, 256>(ldoff, Kh, j * T::BK, N, Kbuf, wave, lane);
+      wait_vmem();
+      zero_tail<D, T::BK, 256>(j * T::BK, N, Kbuf, wave, lane);
+      __syncthreads();
+      if (j < n_wave) {
+        const int kb0 = j * T::BK;
+        scores(Kbuf, sa);
+        if ((kb0 + T::BK > N) || (CAUSAL && kb0 + T::BK - 1 > qw0)) mask(sa, kb0);
+        st.M = track(sa);
+      }
+      __syncthreads();  // the next copy overwrites the tile just read
+    }
+  }
+
+  // ---- prologue: K[jb], V[jb] (and K[jb+1]) into LDS; scores of block jb
+  if (jb < je) {
+    load_tile_async<D, T::BK, 256>(ldoff, Kh, jb * T::BK, N, Kbuf, wave, lane);
+    load_tile_async<D, T::BK, 256>(ldoff, Vh, jb * T::BK, N, Vbuf, wave, lane);
+    if (jb + 1 < je) load_tile_async<D, T::BK, 256>(ldoff, Kh, (jb + 1) * T::BK, N, Kbuf + T::TILE, wave, lane);
+    wait_vmem();
+    wait_vmem_tracked();
+    zero_tail<D, T::BK, 256>(jb * T::BK, N, Kbuf, wave, lane);
+    zero_tail<D, T::BK, 256>(jb * T::BK, N, Vbuf, wave, lane);
+    if (jb + 1 < je) zero_tail<D, T::BK, 256>((jb + 1) * T::BK, N, Kbuf + T::TILE, wave, lane);
+    __syncthreads();
+    if (jb < n_wave) scores(Kbuf, sa);
+    // The first iteration copies block jb+2 into the tile these scores were
+    // just read from; every wave's reads of it must be complete before any
+    // wave issues that copy.
+    if (jb + 2 < je) __syncthreads();
+  }
 
   auto iteration = [&](int j, f32x16* sc, f32x16* sn) {
     // Prefetch: K[j+2] into the K tile block j used, V[j+1] into the V tile
     // block j-1 used; both were released by the barrier that ended j-1.
-    bf16_t* const kdst = Kbuf + (j & 1) * T::TILE;
-    bf16_t* const vdst = Vbuf + ((j + 1) & 1) * T::TILE;
-    if (j + 2 < n_kblk) load_tile_async<D, T::BK, 256>(ldoff, Kh, (j + 2) * T::BK, N, kdst, wave, lane);
-    if (j + 1 < n_kblk) load_tile_async<D, T::BK, 256>(ldoff, Vh, (j + 1) * T::BK, N, vdst, wave, lane);
+    const int jj = j - jb;  // tile slots alternate from the first block of the range
+    bf16_t* const kdst = Kbuf + (jj & 1) * T::TILE;
+    bf16_t* const vdst = Vbuf + ((jj + 1) & 1) * T::TILE;
+    if (j + 2 < je) load_tile_async<D, T::BK, 256>(ldoff, Kh, (j + 2) * T::BK, N, kdst, wave, lane);
+    if (j + 1 < je) load_tile_async<D, T::BK, 256>(ldoff, Vh, (j + 1) * T::BK, N, vdst, wave, lane);
 
     if (j < n_wave) {
       const int kb0 = j * T::BK;
@@ -270,24 +322,42 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
       // overlap the VALU and exponential instructions.  On the wave's last
       // block they read a stale (in-bounds) tile and are discarded.
       bf16x8 pb[NK];
-      scores(Kbuf + ((j + 1) & 1) * T::TILE, sn);
+      scores(Kbuf + ((jj + 1) & 1) * T::TILE, sn);
       softmax(sc, pb);
-      pv(Vbuf + (j & 1) * T::TILE, pb);
+      pv(Vbuf + (jj & 1) * T::TILE, pb);
     }
     wait_vmem();
-    if (j + 2 < n_kblk) zero_tail<D, T::BK, 256>((j + 2) * T::BK, N, kdst, wave, lane);
-    if (j + 1 < n_kblk) zero_tail<D, T::BK, 256>((j + 1) * T::BK, N, vdst, wave, lane);
+    if (j + 2 < je) zero_tail<D, T::BK, 256>((j + 2) * T::BK, N, kdst, wave, lane);
+    if (j + 1 < je) zero_tail<D, T::BK, 256>((j + 1) * T::BK, N, vdst, wave, lane);
     __syncthreads();
   };
-  for (int j = 0; j < n_kblk; j += 2) {
+  for (int j = jb; j < je; j += 2) {
     iteration(j, sa, sb);
-    if (j + 1 < n_kblk) iteration(j + 1, sb, sa);
+    if (j + 1 < je) iteration(j + 1, sb, sa);
   }
 
   // ---- epilogue: O = O_bar / l (as O_bar * (1/l)), LSE = (M + log2 l) ln 2
   float l_lo, l_hi;
   lane_pair(st.l, l_lo, l_hi);
   const float lt = l_lo + l_hi;
+  if (SPLIT) {
+    // partial results of this range: O_bar and l unnormalised, at shift M
+    if (wave_live && myq < N) {
+      const size_t prow = ((size_t)split * BH + bh) * (size_t)N + myq;
+      float* orow = sp.obar + prow * D;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<float4*>(orow + t * 32 + g4 * 8 + 4 * hi) =
+              make_float4(o[t][4 * g4 + 0], o[t][4 * g4 + 1], o[t][4 * g4 + 2], o[t][4 * g4 + 3]);
+      if (hi == 0) {
+        sp.lrow[prow] = lt;
+        sp.mrow[prow] = st.M;
+      }
+    }
+    return;
+  }
   if (wave_live && myq < N) {
     const float rinv = 1.0f / lt;
     bf16_t* Orow = O + hoff + (size_t)myq * D;
@@ -321,9 +391,64 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const long long total = (long long)((BH + G - 1) / G) * G * n_qblk;
   const int remap = (total % 8 == 0) ? 1 : 0;
   const int block_major = total <= kFwdBlockMajorMax ? 1 : 0;
-  hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, STAB, DIAG>), dim3((unsigned)total), dim3(256), 0, stream,
+  hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, STAB, DIAG, false>), dim3((unsigned)total), dim3(256), 0, stream,
                      (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (bf16_t*)a.o, a.lse,
-                     a.row_shifted, a.N, n_qblk, (int)total, remap, scale_log2e(a.scale), BH, G, block_major);
+                     a.row_shifted, a.N, n_qblk, (int)total, remap, scale_log2e(a.scale), BH, G, block_major,
+                     SplitOut{});
+  return hipGetLastError();
+}
+
+// Merge of the key ranges: with M the shift at the end of the last range
+// (that of the whole row) and f_s = 2^(M_s - M), O = bf16(sum_s f_s O_bar_s
+// * (1 / sum_s f_s l_s)) and LSE = (M + log2 l) ln 2, summed over s in
+// order.  One thread per four output columns of a row.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(const float* __restrict__ obar,
+                                                        const float* __restrict__ lrow,
+                                                        const float* __restrict__ mrow, bf16_t* __restrict__ O,
+                                                        float* __restrict__ LSE, long long rows, int splits) {
+  constexpr int TPR = D / 4;
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = t / TPR;
+  const int c = (int)(t % TPR);
+  if (row >= rows) return;
+  const float M = mrow[(size_t)(splits - 1) * rows + row];
+  float l = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int s = 0; s < splits; ++s) {
+    const size_t pr = (size_t)s * rows + row;
+    const float f = exp2_fast(mrow[pr] - M);  // 0 for a range that saw no key (M_s = -inf)
+    l += f * lrow[pr];
+    const float4 x = *reinterpret_cast<const float4*>(obar + pr * D + 4 * c);
+    acc.x += f * x.x;
+    acc.y += f * x.y;
+    acc.z += f * x.z;
+    acc.w += f * x.w;
+  }
+  const float rinv = 1.0f / l;
+  uint2 w;
+  w.x = pack2<__bf16>(acc.x * rinv, acc.y * rinv);
+  w.y = pack2<__bf16>(acc.z * rinv, acc.w * rinv);
+  *reinterpret_cast<uint2*>(O + row * D + 4 * c) = w;
+  if (c == 0) LSE[row] = (M + __builtin_log2f(l)) * kLn2;
+}
+
+template <int D, bool CAUSAL, bool STAB>
+hipError_t launch_split_t(const FwdArgs& a, const SplitArgs& sa, hipStream_t stream) {
+  const int n_qblk = (a.N + kFwdBlockQ - 1) / kFwdBlockQ;
+  const int BH = a.B * a.H;
+  const long long total = (long long)BH * n_qblk * sa.splits;
+  SplitOut sp{sa.obar, sa.lrow, sa.mrow, sa.splits};
+  // one group of all heads, block-major (every head's heaviest block first)
+  hipLaunchKernelGGL((fwd_kernel<__bf16, D, CAUSAL, STAB, false, true>), dim3((unsigned)total), dim3(256), 0,
+                     stream, (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (bf16_t*)a.o, a.lse,
+                     nullptr, a.N, n_qblk, (int)total, 0, scale_log2e(a.scale), BH, BH, 1, sp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long rows = (long long)BH * a.N;
+  const long long threads = rows * (D / 4);
+  hipLaunchKernelGGL((fwd_merge_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                     sa.obar, sa.lrow, sa.mrow, (bf16_t*)a.o, a.lse, rows, sa.splits);
   return hipGetLastError();
 }
 
@@ -347,6 +472,15 @@ float scale_log2e(float scale) { return (float)((double)scale * 1.44269504088896
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
   return a.dtype == kF16 ? launch_fwd_e<_Float16>(a, s) : launch_fwd_e<__bf16>(a, s);
+}
+
+hipError_t launch_fwd_split(const FwdArgs& a, const SplitArgs& sa, hipStream_t s) {
+  if (a.d == 64) {
+    if (a.causal) return a.stabilize ? launch_split_t<64, true, true>(a, sa, s) : launch_split_t<64, true, false>(a, sa, s);
+    return a.stabilize ? launch_split_t<64, false, true>(a, sa, s) : launch_split_t<64, false, false>(a, sa, s);
+  }
+  if (a.causal) return a.stabilize ? launch_split_t<128, true, true>(a, sa, s) : launch_split_t<128, true, false>(a, sa, s);
+  return a.stabilize ? launch_split_t<128, false, true>(a, sa, s) : launch_split_t<128, false, false>(a, sa, s);
 }
 
 }  // namespace fa

@@ -44,6 +44,17 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+// The split-key forward (bf16): partial results of `splits` key ranges in
+// caller-supplied fp32 buffers, then a merge kernel writes O and LSE.
+struct SplitArgs {
+  float* obar;  // (splits, B*H, N, d)
+  float* lrow;  // (splits, B*H, N)
+  float* mrow;  // (splits, B*H, N)
+  int splits;
+};
+constexpr int kMaxSplits = 64;
+hipError_t launch_fwd_split(const FwdArgs& a, const SplitArgs& sa, hipStream_t stream);
 hipError_t launch_bwd_dot(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
