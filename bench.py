@@ -444,7 +444,9 @@ def _timed(fn, reps):
 
 def sweep(args):
     """Forward (fix on, fix off) and backward throughput on every workload,
-    algorithmic FLOP and bytes as in the step benchmark."""
+    algorithmic FLOP and bytes as in the step benchmark; for the bf16
+    workloads also the split-key forward (2, 4 and 8 key ranges, fix on) and
+    the FP32-accumulating baseline."""
     import numpy as np
     import torch
 
@@ -479,6 +481,16 @@ def sweep(args):
         t_on = min(t_on, *(_timed(fon, reps) for _ in range(2)))
         fon()
         t_bwd = min(_timed(bwd, reps) for _ in range(3))
+        t_split = {}
+        if w.dtype == "bf16":
+            ws_s = torch.empty(fa.fwd_split_workspace_bytes(B, H, N, d, 8), dtype=torch.uint8, device="cuda")
+            o_s = torch.empty_like(q)
+            l_s = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+            for ns in (2, 4, 8):
+                fn = lambda ns=ns: fa.fwd_split(q, k, v, ns, causal=w.causal, stabilize=True,  # noqa: E731
+                                                workspace=ws_s, out=o_s, lse=l_s)
+                t_split[ns] = min(_timed(fn, reps) for _ in range(2))
+            del ws_s, o_s, l_s
         t_base = None
         if w.dtype == "bf16":
             ws = torch.empty(fa.base_workspace_bytes(B, H, N, d, w.causal), dtype=torch.uint8, device="cuda")
@@ -498,6 +510,11 @@ def sweep(args):
                "bwd_ms": round(t_bwd, 4),
                "bwd_tflops": round(2.5 * fwd_flop / (t_bwd * 1e-3) / 1e12, 1),
                "bwd_pct_peak": round(100 * 2.5 * fwd_flop / (t_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+        if t_split:
+            best = min(t_split, key=t_split.get)
+            rec["fwd_split_ms"] = {str(n_): round(t_, 4) for n_, t_ in t_split.items()}
+            rec["fwd_split_best"] = {"splits": best, "ms": round(t_split[best], 4),
+                                     "speedup_over_one_pass": round(t_on / t_split[best], 3)}
         if t_base is not None:
             rec["baseline_fp32acc_ms"] = round(t_base, 4)
             rec["flash_speedup_over_baseline"] = round(t_base / t_on, 2)
