@@ -304,6 +304,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
     // wave issues that copy.
     if (jb + 2 < je) __syncthreads();
   }
+  // (On every path into the block loop the compiler must see the prologue's
+  // register loads completed, or it waits for them, and with them for the
+  // loop's tile prefetches, inside the loop.)
+  wait_vmem_tracked();
 
   auto iteration = [&](int j, f32x16* sc, f32x16* sn) {
     // Prefetch: K[j+2] into the K tile block j used, V[j+1] into the V tile
