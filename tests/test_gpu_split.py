@@ -121,3 +121,25 @@ def test_split_removes_the_tie_bias_like_one_pass(fa):
             f"+- {stats[stabilize][1]:.1e}")
     assert stats[False][0] > 4 * stats[False][1]
     assert abs(stats[True][0]) < 0.5 * stats[False][0]
+
+
+@pytest.mark.parametrize("splits", [2, 4])
+def test_split_c4_full_sampled_heads(fa, splits):
+    """Llama-2-7B shape (4, 32, 4096, 128), causal, fix on, at the range counts
+    the sweep times: sampled heads against the exact oracle, and the whole
+    output against fa_fwd."""
+    import torch
+    w = F.WORKLOADS["c4"]
+    say(f"split c4 full splits={splits}")
+    full, dev = device_inputs(w)
+    o, lse = fa.fwd(dev["q"], dev["k"], dev["v"], causal=True, stabilize=True)
+    os_, ls = fa.fwd_split(dev["q"], dev["k"], dev["v"], splits, causal=True, stabilize=True)
+    torch.cuda.synchronize()
+    same = (os_ == o).float().mean().item()
+    assert same >= 0.98, same
+    assert (ls - lse).abs().max().item() <= 1e-5
+    for b, h in F.sample_pairs(w, 2, seed=splits):
+        q, k, v = (head_f64(full[n][b, h]) for n in ("q", "k", "v"))
+        o_ref, _ = REF.forward(q, k, v, w.scale, True)
+        e = Mt.output_errors(to_f64(os_[b, h]), o_ref)
+        assert e["max_abs"] <= MAX_ABS and e["mean_abs"] <= MEAN_ABS, (b, h, e)
