@@ -366,6 +366,6 @@ void fa_fwd_tile(int d, int* block_q, int* block_k) {
   if (block_k) *block_k = ok ? fa::kFwdBlockK : 0;
 }
 
-int fa_version(void) { return 200; }
+int fa_version(void) { return 300; }
 
 }  // extern "C"
