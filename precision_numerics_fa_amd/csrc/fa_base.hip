@@ -245,14 +245,20 @@ __global__ __launch_bounds__(256) void base_softmax_kernel(const float* __restri
 
 // ---------------------------------------------------------------- O = P V
 // O^T = V^T P^T as in the FlashAttention forward: V^T through the
-// transposing LDS read of a swizzled V tile (A operand), the lane's row of P
-// straight from HBM as the B operand, O^T accumulated in FP32 registers.
+// transposing LDS read of a swizzled V tile (A operand), the workgroup's 128
+// rows of P for the block copied straight from HBM into a swizzled LDS tile
+// (whole 128-byte row segments) and read back as the B operand, O^T
+// accumulated in FP32 registers.  V and P tiles are double-buffered.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void base_pv_kernel(const bf16_t* __restrict__ P, const bf16_t* __restrict__ V,
                                                       bf16_t* __restrict__ O, int N, int ld, BaseGrid grid) {
-  constexpr int TILE = kBaseBK * D;
+  constexpr int TILE = kBaseBK * D;         // one V tile (elements)
+  constexpr int PTILE = kBaseBQ * kBaseBK;  // one P tile: 128 rows x 64 keys
+  constexpr int PPER = PTILE / 8 / 256;     // 16-byte copies per lane per P tile
   constexpr int NK = kBaseBK / 16;
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * TILE + 2 * PTILE];
+  bf16_t* const vbuf = smem;
+  bf16_t* const pbuf = smem + 2 * TILE;
   int bh, qb;
   if (!base_block(grid.n_qblk, grid.total, grid.remap, grid.BH, grid.G, bh, qb)) return;
   const int q0 = qb * kBaseBQ;
@@ -261,6 +267,7 @@ __global__ __launch_bounds__(256) void base_pv_kernel(const bf16_t* __restrict__
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const size_t hoff = (size_t)bh * (size_t)N * D;
   const bf16_t* Vh = V + hoff;
+  const bf16_t* Pq = P + ((size_t)bh * (size_t)N + (size_t)q0) * ld;  // row q0 of this head
 
   const int qw0 = q0 + wave * 32;
   const int myq = qw0 + l32;
@@ -268,59 +275,73 @@ __global__ __launch_bounds__(256) void base_pv_kernel(const bf16_t* __restrict__
   const int last_row = min(q0 + kBaseBQ, N) - 1;
   const int n_kblk = CAUSAL ? (last_row / kBaseBK + 1) : (N + kBaseBK - 1) / kBaseBK;
   const int n_wave = !wave_live ? 0 : (CAUSAL ? min(n_kblk, min(qw0 + 31, N - 1) / kBaseBK + 1) : n_kblk);
-  const bf16_t* Prow = P + ((size_t)bh * (size_t)N + (size_t)min(myq, N - 1)) * ld;
 
   // V^T operand of key step ks: slot e of the lane holds key 16 ks + 8 hi + e
-  // (the order in which the lane's row of P is loaded), read as two
-  // transposing reads of rows 8 hi + 0..3 and 8 hi + 4..7.
+  // (the order of the lane's P operand), read as two transposing reads of
+  // rows 8 hi + 0..3 and 8 hi + 4..7.
   const int j16 = lane & 15, dsub = (lane >> 4) & 1;
   const uint32_t vx0 = 2u * (uint32_t)tile_off<D>(8 * hi + (j16 >> 2), 16 * dsub + 4 * (j16 & 3));
   const uint32_t vx1 = 2u * (uint32_t)tile_off<D>(8 * hi + 4 + (j16 >> 2), 16 * dsub + 4 * (j16 & 3));
+  // P operand of key step ks: row 32 wave + l32, keys 16 ks + 8 hi + 0..7
+  // (chunk 2 ks + hi) at offset ^ (ks << 5)
+  const uint32_t px0 = 2u * (uint32_t)tile_off<kBaseBK>(wave * 32 + l32, hi * 8);
   int ldoff[kBaseBK * D / 8 / 256];
   tile_offsets<D, kBaseBK, 256>(ldoff, wave, lane);
+  // P tile copies: copy r of this lane fills physical chunk c = 256 r +
+  // 64 wave + lane, which holds logical chunk (c % 8) ^ swz(row) of row c / 8;
+  // rows past N read row N - 1 (in bounds; those rows' outputs are not kept)
+  uint32_t poff[PPER];
+#pragma unroll
+  for (int r = 0; r < PPER; ++r) {
+    const int c = r * 256 + wave * 64 + lane;
+    const int row = c >> 3;
+    const int lc = (c & 7) ^ swz<kBaseBK>(row);
+    const int src = min(q0 + row, N - 1) - q0;
+    poff[r] = (uint32_t)(((size_t)src * ld + lc * 8) * 2);
+  }
+  auto copy_p = [&](int j, bf16_t* dst) {
+#pragma unroll
+    for (int r = 0; r < PPER; ++r) dma16(Pq + j * kBaseBK, poff[r], lds_addr(dst + (r * 256 + wave * 64) * 8));
+  };
 
   f32x16 o[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) o[t] = zero16();
 
-  load_tile_async<D, kBaseBK, 256>(ldoff, Vh, 0, N, smem, wave, lane);
+  load_tile_async<D, kBaseBK, 256>(ldoff, Vh, 0, N, vbuf, wave, lane);
+  copy_p(0, pbuf);
   wait_vmem();
   wait_vmem_tracked();
-  zero_tail<D, kBaseBK, 256>(0, N, smem, wave, lane);
+  zero_tail<D, kBaseBK, 256>(0, N, vbuf, wave, lane);
   __syncthreads();
 
   for (int j = 0; j < n_kblk; ++j) {
-    bf16_t* const next = smem + ((j + 1) & 1) * TILE;
+    // block j + 1's tiles go into the buffers block j - 1 used (released by
+    // the barrier that ended it)
+    bf16_t* const vnext = vbuf + ((j + 1) & 1) * TILE;
+    if (j + 1 < n_kblk) {
+      load_tile_async<D, kBaseBK, 256>(ldoff, Vh, (j + 1) * kBaseBK, N, vnext, wave, lane);
+      copy_p(j + 1, pbuf + ((j + 1) & 1) * PTILE);
+    }
     if (j < n_wave) {
-      // this lane's probabilities for the block, keys 16 ks + 8 hi + 0..7
-      bf16x8 pb[NK];
+      const bf16_t* Vs = vbuf + (j & 1) * TILE;
+      const char* Ps = reinterpret_cast<const char*>(pbuf + (j & 1) * PTILE);
+      const uint32_t va = (uint32_t)opaque((int)vx0), vb = (uint32_t)opaque((int)vx1);
+      const uint32_t pa = (uint32_t)opaque((int)px0);
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) {
-        if (myq < N) {
-          pb[ks] = *reinterpret_cast<const bf16x8*>(Prow + j * kBaseBK + ks * 16 + hi * 8);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pb[ks][e] = (__bf16)0.0f;
-        }
-      }
-      wait_vmem_tracked();
-      if (j + 1 < n_kblk) load_tile_async<D, kBaseBK, 256>(ldoff, Vh, (j + 1) * kBaseBK, N, next, wave, lane);
-      const bf16_t* Vs = smem + (j & 1) * TILE;
-      const uint32_t va = (uint32_t)opaque((int)vx0), vb = (uint32_t)opaque((int)vx1);
-#pragma unroll
-      for (int ks = 0; ks < NK; ++ks)
+        const bf16x8 pb = lds_load8(reinterpret_cast<const bf16_t*>(Ps + (pa ^ (uint32_t)(ks << 5))));
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           const char* base = reinterpret_cast<const char*>(Vs + ks * 16 * D);
           const bf16x8 a = join8(lds_load_tr4(reinterpret_cast<const bf16_t*>(base + (va ^ (uint32_t)(dt << 6)))),
                                  lds_load_tr4(reinterpret_cast<const bf16_t*>(base + (vb ^ (uint32_t)(dt << 6)))));
-          o[dt] = mfma<__bf16>(a, pb[ks], o[dt]);
+          o[dt] = mfma<__bf16>(a, pb, o[dt]);
         }
-    } else if (j + 1 < n_kblk) {
-      load_tile_async<D, kBaseBK, 256>(ldoff, Vh, (j + 1) * kBaseBK, N, next, wave, lane);
+      }
     }
     wait_vmem();
-    if (j + 1 < n_kblk) zero_tail<D, kBaseBK, 256>((j + 1) * kBaseBK, N, next, wave, lane);
+    if (j + 1 < n_kblk) zero_tail<D, kBaseBK, 256>((j + 1) * kBaseBK, N, vnext, wave, lane);
     __syncthreads();
   }
 
