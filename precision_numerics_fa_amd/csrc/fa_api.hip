@@ -363,7 +363,7 @@ int fa_stabilize_params_ex(int dtype, float* delta_min, float* delta_max, float*
 void fa_fwd_tile(int d, int* block_q, int* block_k) {
   const bool ok = d == 64 || d == 128;
   if (block_q) *block_q = ok ? fa::kFwdBlockQ : 0;
-  if (block_k) *block_k = ok ? fa::kFwdBlockK : 0;
+  if (block_k) *block_k = ok ? fa::fwd_block_k(d) : 0;
 }
 
 int fa_version(void) { return 300; }

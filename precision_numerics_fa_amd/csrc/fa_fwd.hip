@@ -42,9 +42,14 @@ namespace {
 
 template <int D>
 struct FwdTile {
-  static constexpr int BQ = kFwdBlockQ;  // query rows per workgroup (4 waves x 32)
-  static constexpr int BK = kFwdBlockK;  // keys per block
-  static constexpr int TILE = BK * D;    // one swizzled K or V tile (elements)
+  static constexpr int BQ = kFwdBlockQ;      // query rows per workgroup (4 waves x 32)
+  static constexpr int BK = fwd_block_k(D);  // keys per block
+  static constexpr int TILE = BK * D;        // one swizzled K or V tile (elements)
+  // Sequential blocks (d = 64): one K and one V tile; K[j+1] lands during
+  // block j's softmax and products, V[j] during its scores.  Otherwise two
+  // of each, and the next block's scores overlap this block's softmax.
+  static constexpr bool SEQ = BK == 128;
+  static constexpr int NTILES = SEQ ? 2 : 4;
 };
 
 // Per-wave softmax state of 32 query rows (one row per lane pair).
@@ -78,11 +83,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   using T = FwdTile<D>;
   constexpr int NS = T::BK / 32;   // 32-key subtiles per block
   constexpr int NK = T::BK / 16;   // 16-key MFMA steps per block
-  // two K tiles and two V tiles: K[j+1] and V[j] are read while K[j+2] and
-  // V[j+1] land (direct global -> LDS loads)
-  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * T::TILE];
+  // d = 128: two K tiles and two V tiles (K[j+1] and V[j] are read while
+  // K[j+2] and V[j+1] land); d = 64: one of each (direct global -> LDS loads)
+  __shared__ __attribute__((aligned(16))) bf16_t smem[T::NTILES * T::TILE];
   bf16_t* const Kbuf = smem;
-  bf16_t* const Vbuf = smem + 2 * T::TILE;
+  bf16_t* const Vbuf = smem + (T::NTILES / 2) * T::TILE;
 
   // Workgroup -> (head, query block).  The hardware hands workgroup i to XCD
   // i % 8; the remap gives each XCD a contiguous range of the order below.
@@ -287,57 +292,98 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
     }
   }
 
-  // ---- prologue: K[jb], V[jb] (and K[jb+1]) into LDS; scores of block jb
-  if (jb < je) {
-    load_tile_async<D, T::BK, 256>(ldoff, Kh, jb * T::BK, N, Kbuf, wave, lane);
-    load_tile_async<D, T::BK, 256>(ldoff, Vh, jb * T::BK, N, Vbuf, wave, lane);
-    if (jb + 1 < je) load_tile_async<D, T::BK, 256>(ldoff, Kh, (jb + 1) * T::BK, N, Kbuf + T::TILE, wave, lane);
-    wait_vmem();
-    wait_vmem_tracked();
-    zero_tail<D, T::BK, 256>(jb * T::BK, N, Kbuf, wave, lane);
-    zero_tail<D, T::BK, 256>(jb * T::BK, N, Vbuf, wave, lane);
-    if (jb + 1 < je) zero_tail<D, T::BK, 256>((jb + 1) * T::BK, N, Kbuf + T::TILE, wave, lane);
-    __syncthreads();
-    if (jb < n_wave) scores(Kbuf, sa);
-    // The first iteration copies block jb+2 into the tile these scores were
-    // just read from; every wave's reads of it must be complete before any
-    // wave issues that copy.
-    if (jb + 2 < je) __syncthreads();
-  }
-  // (On every path into the block loop the compiler must see the prologue's
-  // register loads completed, or it waits for them, and with them for the
-  // loop's tile prefetches, inside the loop.)
-  wait_vmem_tracked();
-
-  auto iteration = [&](int j, f32x16* sc, f32x16* sn) {
-    // Prefetch: K[j+2] into the K tile block j used, V[j+1] into the V tile
-    // block j-1 used; both were released by the barrier that ended j-1.
-    const int jj = j - jb;  // tile slots alternate from the first block of the range
-    bf16_t* const kdst = Kbuf + (jj & 1) * T::TILE;
-    bf16_t* const vdst = Vbuf + ((jj + 1) & 1) * T::TILE;
-    if (j + 2 < je) load_tile_async<D, T::BK, 256>(ldoff, Kh, (j + 2) * T::BK, N, kdst, wave, lane);
-    if (j + 1 < je) load_tile_async<D, T::BK, 256>(ldoff, Vh, (j + 1) * T::BK, N, vdst, wave, lane);
-
-    if (j < n_wave) {
-      const int kb0 = j * T::BK;
-      if ((kb0 + T::BK > N) || (CAUSAL && kb0 + T::BK - 1 > qw0)) mask(sc, kb0);
-      // The scores of the next block are issued together with this block's
-      // softmax: independent work in one basic block, so the MFMAs can
-      // overlap the VALU and exponential instructions.  On the wave's last
-      // block they read a stale (in-bounds) tile and are discarded.
-      bf16x8 pb[NK];
-      scores(Kbuf + ((jj + 1) & 1) * T::TILE, sn);
-      softmax(sc, pb);
-      pv(Vbuf + (jj & 1) * T::TILE, pb);
+  if constexpr (T::SEQ) {
+    // ---- sequential blocks: K[j] is in LDS when block j starts
+    if (jb < je) {
+      load_tile_async<D, T::BK, 256>(ldoff, Kh, jb * T::BK, N, Kbuf, wave, lane);
+      wait_vmem();
+      zero_tail<D, T::BK, 256>(jb * T::BK, N, Kbuf, wave, lane);
+      __syncthreads();
     }
-    wait_vmem();
-    if (j + 2 < je) zero_tail<D, T::BK, 256>((j + 2) * T::BK, N, kdst, wave, lane);
-    if (j + 1 < je) zero_tail<D, T::BK, 256>((j + 1) * T::BK, N, vdst, wave, lane);
-    __syncthreads();
-  };
-  for (int j = jb; j < je; j += 2) {
-    iteration(j, sa, sb);
-    if (j + 1 < je) iteration(j + 1, sb, sa);
+    // (on every path into the block loop the compiler must see the
+    // prologue's register loads completed, or it waits for them, and with
+    // them for the loop's tile copies, inside the loop)
+    wait_vmem_tracked();
+    constexpr int KPER = T::BK * D / 8 / 256;  // 16-byte copies per lane of one tile
+    for (int j = jb; j < je; ++j) {
+      const bool live = j < n_wave;
+      const int kb0 = j * T::BK;
+      // V[j] into the V tile, whose reads of block j-1 ended at its last barrier
+      load_tile_async<D, T::BK, 256>(ldoff, Vh, kb0, N, Vbuf, wave, lane);
+      if (live) {
+        scores(Kbuf, sa);
+        if ((kb0 + T::BK > N) || (CAUSAL && kb0 + T::BK - 1 > qw0)) mask(sa, kb0);
+      }
+      __syncthreads();  // every wave's reads of K[j] are done
+      if (j + 1 < je) load_tile_async<D, T::BK, 256>(ldoff, Kh, kb0 + T::BK, N, Kbuf, wave, lane);
+      bf16x8 pb[NK];
+      if (live) softmax(sa, pb);
+      // V[j]'s copies were issued before K[j+1]'s, and loads complete in order
+      if (j + 1 < je) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KPER) : "memory");
+      } else {
+        wait_vmem();
+      }
+      zero_tail<D, T::BK, 256>(kb0, N, Vbuf, wave, lane);
+      __syncthreads();  // V[j] complete for every wave
+      if (live) pv(Vbuf, pb);
+      wait_vmem();
+      if (j + 1 < je) zero_tail<D, T::BK, 256>(kb0 + T::BK, N, Kbuf, wave, lane);
+      __syncthreads();  // K[j+1] complete; every wave's reads of V[j] are done
+    }
+  } else {
+    // ---- prologue: K[jb], V[jb] (and K[jb+1]) into LDS; scores of block jb
+    if (jb < je) {
+      load_tile_async<D, T::BK, 256>(ldoff, Kh, jb * T::BK, N, Kbuf, wave, lane);
+      load_tile_async<D, T::BK, 256>(ldoff, Vh, jb * T::BK, N, Vbuf, wave, lane);
+      if (jb + 1 < je) load_tile_async<D, T::BK, 256>(ldoff, Kh, (jb + 1) * T::BK, N, Kbuf + T::TILE, wave, lane);
+      wait_vmem();
+      wait_vmem_tracked();
+      zero_tail<D, T::BK, 256>(jb * T::BK, N, Kbuf, wave, lane);
+      zero_tail<D, T::BK, 256>(jb * T::BK, N, Vbuf, wave, lane);
+      if (jb + 1 < je) zero_tail<D, T::BK, 256>((jb + 1) * T::BK, N, Kbuf + T::TILE, wave, lane);
+      __syncthreads();
+      if (jb < n_wave) scores(Kbuf, sa);
+      // The first iteration copies block jb+2 into the tile these scores were
+      // just read from; every wave's reads of it must be complete before any
+      // wave issues that copy.
+      if (jb + 2 < je) __syncthreads();
+    }
+    // (On every path into the block loop the compiler must see the prologue's
+    // register loads completed, or it waits for them, and with them for the
+    // loop's tile prefetches, inside the loop.)
+    wait_vmem_tracked();
+
+    auto iteration = [&](int j, f32x16* sc, f32x16* sn) {
+      // Prefetch: K[j+2] into the K tile block j used, V[j+1] into the V tile
+      // block j-1 used; both were released by the barrier that ended j-1.
+      const int jj = j - jb;  // tile slots alternate from the first block of the range
+      bf16_t* const kdst = Kbuf + (jj & 1) * T::TILE;
+      bf16_t* const vdst = Vbuf + ((jj + 1) & 1) * T::TILE;
+      if (j + 2 < je) load_tile_async<D, T::BK, 256>(ldoff, Kh, (j + 2) * T::BK, N, kdst, wave, lane);
+      if (j + 1 < je) load_tile_async<D, T::BK, 256>(ldoff, Vh, (j + 1) * T::BK, N, vdst, wave, lane);
+
+      if (j < n_wave) {
+        const int kb0 = j * T::BK;
+        if ((kb0 + T::BK > N) || (CAUSAL && kb0 + T::BK - 1 > qw0)) mask(sc, kb0);
+        // The scores of the next block are issued together with this block's
+        // softmax: independent work in one basic block, so the MFMAs can
+        // overlap the VALU and exponential instructions.  On the wave's last
+        // block they read a stale (in-bounds) tile and are discarded.
+        bf16x8 pb[NK];
+        scores(Kbuf + ((jj + 1) & 1) * T::TILE, sn);
+        softmax(sc, pb);
+        pv(Vbuf + (jj & 1) * T::TILE, pb);
+      }
+      wait_vmem();
+      if (j + 2 < je) zero_tail<D, T::BK, 256>((j + 2) * T::BK, N, kdst, wave, lane);
+      if (j + 1 < je) zero_tail<D, T::BK, 256>((j + 1) * T::BK, N, vdst, wave, lane);
+      __syncthreads();
+    };
+    for (int j = jb; j < je; j += 2) {
+      iteration(j, sa, sb);
+      if (j + 1 < je) iteration(j + 1, sb, sa);
+    }
   }
 
   // ---- epilogue: O = O_bar / l (as O_bar * (1/l)), LSE = (M + log2 l) ln 2

@@ -98,6 +98,9 @@ constexpr int kHbmProbeBlocks = 4096;
 hipError_t launch_read_probe(const void* src, uint32_t* sink, long long n16, hipStream_t stream);
 
 constexpr int kFwdBlockQ = 128;
-constexpr int kFwdBlockK = 64;
+// Keys per block of the forward: 128 for d = 64 (one K and one V tile, the
+// block's products after its softmax), 64 for d = 128 (two of each, the next
+// block's scores issued with this block's softmax).
+constexpr int fwd_block_k(int d) { return d == 64 ? 128 : 64; }
 
 }  // namespace fa
