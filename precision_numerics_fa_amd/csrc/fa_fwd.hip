@@ -76,7 +76,7 @@ struct SplitOut {
 // the same shift and the same rounding of P, as in one pass; it then writes
 // its unnormalised output, row sum and final shift for the merge kernel.
 template <typename E, int D, bool CAUSAL, bool STAB, bool DIAG, bool SPLIT>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(
+__global__ __launch_bounds__(256, FwdTile<D>::SEQ ? 3 : 2) void fwd_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     bf16_t* __restrict__ O, float* __restrict__ LSE, uint8_t* __restrict__ row_shifted,
     int N, int n_qblk, int total_blocks, int xcd_remap, float c2, int BH, int G, int block_major, SplitOut sp) {
