@@ -117,7 +117,7 @@ def test_shift_rule_values():
 
 @pytest.mark.parametrize("stabilize", [False, True])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("block", [1, 7, 16, 64, 256])
+@pytest.mark.parametrize("block", [1, 7, 16, 64, 128, 256])
 def test_no_round_equals_exact_oracle(block, causal, stabilize):
     w, (q, k, v), _ = _head("c1", causal=causal, N=200)
     o, lse = A.forward(q, k, v, w.scale, causal)
@@ -141,7 +141,7 @@ def test_no_round_backward_equals_exact_oracle():
 @pytest.mark.parametrize("name", ["c1", "c2", "c5"])
 def test_running_count_equals_brute_force_count(name):
     w, (q, k, v), hd = _head(name, N=256) if name != "c1" else _head(name)
-    for block in (16, 64):
+    for block in (16, 64, 128):
         _, _, st = B.forward(q, k, v, w.scale, w.causal, block=block, stabilize=True, return_state=True)
         # brute force on the same fp32 raw scores the emulation uses
         t = B.fl32(q @ k.T)
@@ -155,11 +155,12 @@ def test_running_count_equals_brute_force_count(name):
         assert set(np.flatnonzero(exact >= 2)) == set(hd["tie_rows"].tolist())
 
 
+@pytest.mark.parametrize("block", [64, 128])
 @pytest.mark.parametrize("name", ["c1", "c2"])
-def test_fix_acts_only_on_repeated_max_and_stays_below_one(name):
+def test_fix_acts_only_on_repeated_max_and_stays_below_one(name, block):
     w, (q, k, v), hd = _head(name, N=512) if name == "c2" else _head(name)
-    o0, l0, s0 = B.forward(q, k, v, w.scale, w.causal, block=64, stabilize=False, return_state=True)
-    o1, l1, s1 = B.forward(q, k, v, w.scale, w.causal, block=64, stabilize=True, return_state=True)
+    o0, l0, s0 = B.forward(q, k, v, w.scale, w.causal, block=block, stabilize=False, return_state=True)
+    o1, l1, s1 = B.forward(q, k, v, w.scale, w.causal, block=block, stabilize=True, return_state=True)
     never = ~s1["ever_shifted"]
     assert never.sum() > 0 and (~never).sum() >= len(hd["tie_rows"])
     assert np.array_equal(o0[never], o1[never])
