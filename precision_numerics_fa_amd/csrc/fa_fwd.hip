@@ -13,9 +13,11 @@
 // maximum is strictly below 1 (the rule is in fa_device.hpp).
 //
 // Mapping onto CDNA4.  A workgroup of 4 waves owns 128 query rows, 32 per
-// wave; keys arrive in blocks of 64.  K and V tiles are copied straight from
-// HBM into swizzled LDS tiles (global_load_lds_dwordx4, no register staging),
-// two blocks ahead for K and one ahead for V, with one barrier per block.
+// wave; keys arrive in blocks of 64 (d = 128) or 128 (d = 64).  K and V
+// tiles are copied straight from HBM into swizzled LDS tiles
+// (global_load_lds_dwordx4, no register staging): at d = 128 two blocks ahead
+// for K and one ahead for V, with one barrier per block; at d = 64 one tile
+// of each, K[j+1] landing during block j's softmax and products.
 // Scores are formed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16: K
 // rows come from LDS as the A operand, the wave's Q rows stay in registers as
 // the B operand, and each lane ends up owning one query row (lanes l and l+32
@@ -23,9 +25,10 @@
 // in-lane work plus one exchange with lane l^32, and the BF16 probabilities
 // are already laid out as the B operand of O^T = V^T P^T: no LDS round trip
 // for P.  V^T is read from the row-major V tile with the gfx950 transposing
-// LDS read.  O^T and l stay in registers until the epilogue.  The scores of
-// block j+1 are issued in the same basic block as the softmax of block j, so
-// the MFMAs of one overlap the VALU/exponential work of the other.
+// LDS read.  O^T and l stay in registers until the epilogue.  At d = 128 the
+// scores of block j+1 are issued in the same basic block as the softmax of
+// block j, so the MFMAs of one overlap the VALU/exponential work of the
+// other; at d = 64 that overlap comes from the other waves on the SIMD.
 //
 // Workgroups map to (head, query block) in per-XCD head groups, head-major
 // or, for small launches, block-major (see the kernel's first lines).
