@@ -38,3 +38,14 @@ def random_case(B, H, N, d, seed, mult=1.0, with_do=False, dtype="bf16"):
     names = ["q", "k", "v"] + (["do"] if with_do else [])
     bits = {n: F.random_bf16((B, H, N, d), seed * 10 + i, mult, dtype) for i, n in enumerate(names)}
     return bits, {n: to_dev(b, dtype) for n, b in bits.items()}
+
+
+def lse_err(got, ref) -> float:
+    """Largest LSE error, absolute where |LSE| <= 1 and relative above (fp32
+    LSE of peaked rows is large, and its spacing grows with it)."""
+    got, ref = np.asarray(got, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    return float((np.abs(got - ref) / np.maximum(1.0, np.abs(ref))).max())
+
+
+# LSE gate: the measured errors are ~1.5e-6 (fp32 log2 / exp2 of the kernels)
+LSE_TOL = 1e-5

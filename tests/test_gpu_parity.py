@@ -19,7 +19,7 @@ from oracle import emulation as EMU
 from oracle import metrics as Mt
 from oracle import reference as REF
 
-from gpu_util import device_inputs, head_f64, random_case, say, to_dev, to_f64
+from gpu_util import device_inputs, head_f64, random_case, say, to_dev, to_f64, LSE_TOL, lse_err
 
 pytestmark = pytest.mark.gpu
 
@@ -71,7 +71,7 @@ def test_fwd_small_against_oracle(fa, B, H, N, d, causal, stabilize):
     q, k, v = (head_f64(bits[n]) for n in ("q", "k", "v"))
     o_ref, lse_ref = REF.forward(q, k, v, scale, causal)
     _gate_o(to_f64(o), o_ref)
-    assert np.abs(to_f64(lse) - lse_ref).max() <= 1e-4
+    assert lse_err(to_f64(lse), lse_ref) <= LSE_TOL
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -189,6 +189,21 @@ def test_forward_and_backward_are_deterministic(fa):
         assert torch.equal(a, b)
 
 
+def test_forward_is_deterministic_at_the_c3_shape(fa):
+    """Regression for a forward race (a tile copy into the K tile block 0's
+    scores were still read from) that once showed as a 0.05 output
+    difference at this shape: 64 x 16 x 2048 x 64, causal.  Two calls, fix
+    on, compared bitwise, and the same with the fix off."""
+    import torch
+    say("invariant: determinism at 64x16x2048x64 causal")
+    w = F.WORKLOADS["c3"]
+    full, dev = device_inputs(w)
+    for stab in (True, False):
+        o1, l1 = fa.fwd(dev["q"], dev["k"], dev["v"], causal=True, stabilize=stab)
+        o2, l2 = fa.fwd(dev["q"], dev["k"], dev["v"], causal=True, stabilize=stab)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), stab
+
+
 def test_fix_touches_only_rows_with_a_repeated_maximum(fa):
     """Rows the kernel never shifted are bitwise identical with the fix on and
     off; every row with an exact repeated maximum was shifted."""
@@ -222,7 +237,7 @@ def test_c1_full(fa, stabilize):
     q, k, v = (head_f64(full[n]) for n in ("q", "k", "v"))
     o_ref, lse_ref = REF.forward(q, k, v, w.scale, w.causal)
     e = _gate_o(to_f64(o), o_ref)
-    assert np.abs(to_f64(lse) - lse_ref).max() <= 1e-5
+    assert lse_err(to_f64(lse), lse_ref) <= LSE_TOL
     meta = REF.tie_metadata(q, k, v, w.scale, w.causal)
     say("  c1 errors", e, "ties", _tie_stats(to_f64(o), o_ref, meta)["tie_rows"])
 
@@ -243,7 +258,7 @@ def test_c2_full_and_tie_bias(fa):
             q, k, v = (head_f64(full[n][b]) for n in ("q", "k", "v"))
             o_ref, lse_ref = REF.forward(q, k, v, w.scale, True)
             _gate_o(of[b], o_ref, loose_format=True)
-            assert np.abs(lf[b] - lse_ref).max() <= 1e-4
+            assert lse_err(lf[b], lse_ref) <= LSE_TOL
             meta = REF.tie_metadata(q, k, v, w.scale, True)
             stats.append((of[b] - o_ref, np.sign(o_ref - meta["tie_mean"]), meta["count"] >= 2))
         d = np.concatenate([s[0][s[2]] for s in stats])
@@ -268,7 +283,7 @@ def test_c3_full_sampled_heads(fa, stabilize):
         q, k, v = (head_f64(full[n][b, h]) for n in ("q", "k", "v"))
         o_ref, lse_ref = REF.forward(q, k, v, w.scale, True)
         _gate_o(to_f64(o[b, h]), o_ref)
-        assert np.abs(lse[b, h].cpu().numpy() - lse_ref).max() <= 1e-4
+        assert lse_err(lse[b, h].cpu().numpy(), lse_ref) <= LSE_TOL
 
 
 @pytest.mark.parametrize("stabilize", [False, True])
@@ -283,18 +298,40 @@ def test_c4_full_sampled_heads(fa, stabilize):
         o_ref, lse_ref = REF.forward(q, k, v, w.scale, True)
         e = _gate_o(to_f64(o[b, h]), o_ref)
         worst = max(worst, e["max_rel_normwise"])
-        assert np.abs(lse[b, h].cpu().numpy() - lse_ref).max() <= 1e-4
+        assert lse_err(lse[b, h].cpu().numpy(), lse_ref) <= LSE_TOL
     say(f"  c4 stabilize={stabilize} max relative error (normwise) {worst:.3e}")
 
 
-def test_c5_full_forward_backward_sampled_heads(fa):
-    w = F.WORKLOADS["c5"]
-    say("c5 forward+backward (full size, 16 sampled heads)")
+def test_c4_full_backward_sampled_heads(fa):
+    """The d = 128 backward at full length (B=4, H=32, N=4096, causal): 128
+    query and key blocks per head, in the launch the benchmark times; the
+    Q and K gradients inherit the forward's errors through D and dS (page 1,
+    section 4.3).  dO ~ N(0, 1), drawn after V from the same per-head stream
+    (the c4 recipe with the backward's tensor)."""
+    w = F.WORKLOADS["c4"].with_shape(with_do=True)
+    say("c4 forward+backward (full size, 8 sampled heads)")
     full, dev = device_inputs(w)
     o, lse = fa.fwd(dev["q"], dev["k"], dev["v"], causal=True, stabilize=True)
     dq, dk, dv = fa.bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=True)
     worst = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
-    for (b, h) in F.sample_pairs(w, 16):
+    for (b, h) in F.sample_pairs(w, 8, seed=4):
+        q, k, v, do = (head_f64(full[n][b, h]) for n in ("q", "k", "v", "do"))
+        rq, rk, rv = REF.backward(q, k, v, do, w.scale, True)
+        for name, g, r in (("dq", dq[b, h], rq), ("dk", dk[b, h], rk), ("dv", dv[b, h], rv)):
+            rel = Mt.relative_fro(to_f64(g), r)
+            worst[name] = max(worst[name], rel)
+            assert rel <= GRAD_REL, (name, b, h, rel)
+    say("  c4 worst relative gradient errors", worst)
+
+
+def test_c5_full_forward_backward_every_head(fa):
+    w = F.WORKLOADS["c5"]
+    say("c5 forward+backward (full size, all 256 heads)")
+    full, dev = device_inputs(w)
+    o, lse = fa.fwd(dev["q"], dev["k"], dev["v"], causal=True, stabilize=True)
+    dq, dk, dv = fa.bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=True)
+    worst = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    for (b, h) in [(b, h) for b in range(w.B) for h in range(w.H)]:
         q, k, v, do = (head_f64(full[n][b, h]) for n in ("q", "k", "v", "do"))
         o_ref, _ = REF.forward(q, k, v, w.scale, True)
         _gate_o(to_f64(o[b, h]), o_ref)

@@ -243,6 +243,16 @@ def test_hand_worked_tie_midpoint():
     fq, fk = np.array(g["fold_q"]), np.array(g["fold_k"])
     _, _, st = B.forward(fq, fk, v, g["scale"], False, block=64, stabilize=True, return_state=True)
     assert st["shift"][0] == np.float32(g["fold_R"] + g["fold_delta"])
+    # the shifts, outputs and LSE the GPU check of this example compares against
+    for qq, key, lse_key in ((q, "", "lse"), (-q, "neg_", "neg_lse"), (fq, "fold_", "fold_lse")):
+        kk = fk if key == "fold_" else k
+        for stab, suffix in ((False, "fix_off"), (True, "fix_on")):
+            o_s, l_s, st = B.forward(qq, kk, v, g["scale"], False, block=64, stabilize=stab, return_state=True)
+            assert st["shift"][0] == g[key + "M_" + suffix]
+            if key:
+                assert abs(l_s[0] - g[lse_key]) <= 4e-6
+            if key == "fold_":
+                assert o_s[0, 0] == g["fold_o_" + suffix]
 
 
 def test_hand_worked_tie_midpoint_f16():
@@ -275,3 +285,54 @@ def test_binary16_rule_keeps_the_largest_probability_representable():
                             delta_max=B.DELTA_MAX, fold=B.FOLD)
     assert (st2["pmax_shifted_bf16"][shifted] == 0.0).any()
     assert np.abs(bad - o).max() > 0.1
+
+
+def _bwd_golden():
+    g = json.load(open(os.path.join(GOLDEN, "backward_rounding_sites.json")))
+    return g, {n: np.array(g[n], dtype=np.float64) for n in ("q", "k", "v", "o", "do", "lse")}
+
+
+def test_hand_worked_backward_rounding_sites():
+    """tests/golden/backward_rounding_sites.json: bf16(P) into dV, bf16(dS)
+    into dK and dQ, and D from the bf16 forward output, each visible in the
+    result (page 1, section 4.3)."""
+    g, a = _bwd_golden()
+    dq, dk, dv = B.backward(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], g["scale"], False)
+    assert np.array_equal(dq, np.array(g["dq"]))
+    assert np.array_equal(dk, np.array(g["dk"]))
+    assert np.array_equal(dv, np.array(g["dv"]))
+    # the example's probabilities are the fp32 value it states
+    t = a["q"] @ a["k"].T
+    assert (t == 0.0).all() and B.fl32(2.0 ** -0.5) == g["p_fp32"]
+    # D taken from the exact output (v0 + v1) / 2 instead of the bf16 O: dK_0 is no longer 0
+    o_exact = A.forward(a["q"], a["k"], a["v"], g["scale"], False)[0]
+    assert o_exact[0, 0] == 1.00390625
+    _, dk_x, _ = B.backward(a["q"], a["k"], a["v"], o_exact, a["do"], a["lse"], g["scale"], False)
+    assert dk_x[0, 0] != 0.0
+
+
+@pytest.mark.parametrize("skip, tensor, value", [(1, "dv", "dv_without_p_cast"),
+                                                 (3, "dk", "dk1_without_ds_cast"),
+                                                 (5, "dq", "dk1_without_ds_cast")])
+def test_backward_golden_catches_a_dropped_rounding_site(monkeypatch, skip, tensor, value):
+    """Plant each mistake in the oracle: make the n-th 16-bit rounding of the
+    backward a no-op (call 1 is bf16(P) for dV, 3 and 5 are bf16(dS) for dK
+    and dQ; the even calls round the results) and check that the golden
+    example then fails exactly where its derivation says."""
+    g, a = _bwd_golden()
+    real = B._rounders
+
+    def planted(no_round, fmt="bf16"):
+        r32, rb = real(no_round, fmt)
+        calls = [0]
+
+        def rb_planted(x):
+            calls[0] += 1
+            return np.asarray(x, dtype=np.float64) if calls[0] == skip else rb(x)
+        return r32, rb_planted
+
+    monkeypatch.setattr(B, "_rounders", planted)
+    dq, dk, dv = B.backward(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], g["scale"], False)
+    got = {"dq": dq[0, 1], "dk": dk[1, 0], "dv": dv[0, 0]}[tensor]
+    assert got == g[value]
+    assert got != {"dq": g["dq"][0][1], "dk": g["dk"][1][0], "dv": g["dv"][0][0]}[tensor]
