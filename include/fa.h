@@ -104,7 +104,11 @@ int fa_fwd_diag(const void* Q, const void* K, const void* V, void* O, float* LSE
  * product per range instead of one per block); with splits = 1 the result
  * is bitwise fa_fwd's.  bf16 tensors as in fa_fwd; 1 <= splits <= 64; the
  * workspace (256-byte aligned) holds at least
- * fa_fwd_split_workspace_bytes() bytes.  Two launches. */
+ * fa_fwd_split_workspace_bytes() bytes.  Two launches.  On return the
+ * workspace holds each range's partial results, fp32, each part starting at
+ * the next multiple of 256 bytes: O_bar (splits, B, H, N, d), then
+ * l (splits, B, H, N), then the shift M (splits, B, H, N) in base-2 units
+ * (range splits-1 holds the row's final shift). */
 size_t fa_fwd_split_workspace_bytes(int B, int H, int N, int d, int splits);
 int fa_fwd_split(const void* Q, const void* K, const void* V, void* O, float* LSE,
                  int splits, void* workspace, size_t workspace_bytes,
@@ -116,7 +120,17 @@ int fa_fwd_split(const void* Q, const void* K, const void* V, void* O, float* LS
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int causal);
 
 /* Backward pass (dQ, dK, dV of L = sum(O * dO)), recomputing the
- * probabilities from LSE.
+ * probabilities from LSE.  Page 1, section 4.3: once the forward's softmax
+ * output is off, the gradients with respect to Q and K that back-propagation
+ * relies on are off the true derivatives too; here that happens through
+ * D = rowsum(dO * O), taken from the bf16 forward output, and through
+ * dS = P (dP - D).  The recipe is the usual tiled one for exact attention
+ * (page 3, "Flash Attention: from academic breakthrough to industry
+ * standard": the N x N matrices are never stored, so they are recomputed
+ * block by block):
+ *   P = exp(S - LSE) (FP32),  dP = dO V^T,  dS = P (dP - D),
+ *   dV = bf16(P)^T dO,  dK = scale bf16(dS)^T Q,  dQ = scale bf16(dS) K,
+ * with FP32 accumulation and bf16 results.
  *   in : Q, K, V, O, dO   bf16 (B,H,N,d); O is the forward's bf16 output
  *        LSE              fp32 (B,H,N) from fa_fwd
  *        workspace        device memory of at least fa_bwd_workspace_bytes()
