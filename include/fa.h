@@ -63,7 +63,8 @@ typedef enum {
   FA_ERR_UNSUPPORTED = -2,   /* head dimension other than 64 / 128; baseline N > 16384 */
   FA_ERR_WORKSPACE = -3,     /* workspace NULL or smaller than fa_bwd_workspace_bytes() */
   FA_ERR_LAUNCH = -4,        /* the HIP runtime rejected a kernel launch */
-  FA_ERR_DEVICE = -5         /* no gfx950 device current, or a device query failed */
+  FA_ERR_DEVICE = -5,        /* no gfx950 device current, or a device query failed */
+  FA_ERR_TOO_LARGE = -6      /* B*H*N above fa_bwd_noalloc's fixed scratch (FA_BWD_NOALLOC_MAX_ROWS) */
 } fa_status;
 
 /* Forward pass.
@@ -142,6 +143,26 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
            void* workspace, size_t workspace_bytes,
            int B, int H, int N, int d, int causal, float scale, int stabilize,
            void* stream);
+
+/* Backward pass that allocates nothing, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  It computes exactly what fa_bwd computes,
+ * with the same kernels and bitwise the same dQ, dK and dV, but keeps the
+ * fp32 vector D = rowsum(dO*O) in a scratch array of the library instead of
+ * a caller workspace.  That array is a fixed device array of
+ * FA_BWD_NOALLOC_MAX_ROWS floats (16 MiB) on every GPU the library runs on,
+ * held until the process ends; its address on a device is looked up on the
+ * first call made with that device current.  B*H*N above
+ * FA_BWD_NOALLOC_MAX_ROWS returns FA_ERR_TOO_LARGE before anything is
+ * enqueued.  Every call on one GPU uses that GPU's one array: two calls that
+ * may overlap on the same GPU (different streams, or threads that do not
+ * order their calls) race on it, and the caller must serialise them.
+ * Arguments, layouts and launches otherwise as in fa_bwd (bf16 tensors). */
+#define FA_BWD_NOALLOC_MAX_ROWS 4194304
+int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                   const float* LSE, void* dQ, void* dK, void* dV,
+                   int B, int H, int N, int d, int causal, float scale, int stabilize,
+                   void* stream);
 
 /* The steps of fa_bwd, exposed so that each can be timed on its own.
  *   fa_bwd_dot  : Dvec[b,h,i] = sum_t dO[b,h,i,t] * O[b,h,i,t]   (fp32 out)

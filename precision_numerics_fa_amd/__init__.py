@@ -36,6 +36,8 @@ from ._lib import (  # noqa: F401
     bwd_grads,
     bwd_dkdv,
     bwd_dot,
+    bwd_noalloc,
+    NOALLOC_MAX_ROWS,
     bwd_dq,
     fwd,
     fwd_diag,

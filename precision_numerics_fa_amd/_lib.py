@@ -20,6 +20,7 @@ _SIGNATURES = {
     "fa_fwd_diag": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_dot": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "fa_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
@@ -228,6 +229,32 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None
     _call("fa_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
           _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, N, d, int(bool(causal)),
           _scale(scale, d), int(bool(stabilize)), _stream())
+    return dq, dk, dv
+
+
+# Rows of D (B*H*N) the allocation-free backward's fixed scratch holds.
+NOALLOC_MAX_ROWS = 4194304
+
+
+def bwd_noalloc(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
+                stabilize: bool = False, dq=None, dk=None, dv=None):
+    """Backward pass through fa_bwd_noalloc: no workspace, D in the library's
+    fixed per-device scratch (B*H*N <= NOALLOC_MAX_ROWS).  Calls that may
+    overlap on one GPU race on that scratch.  Returns (dQ, dK, dV); pass
+    preallocated dq, dk, dv to make the call allocate nothing at all."""
+    torch = _torch()
+    B, H, N, d = _shape(q)
+    dev = q.device
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(n, t, torch.bfloat16, (B, H, N, d), dev)
+    _check("lse", lse, torch.float32, (B, H, N), dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(n, t, torch.bfloat16, (B, H, N, d), dev)
+    _call("fa_bwd_noalloc", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+          _ptr(dv), B, H, N, d, int(bool(causal)), _scale(scale, d), int(bool(stabilize)), _stream())
     return dq, dk, dv
 
 

@@ -5,10 +5,17 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
+
+// Scratch of fa_bwd_noalloc: the D vector, one fixed array per device.  The
+// name is only a host-side handle; the device address is looked up once per
+// device (with that device current) and cached, and only that address is
+// ever handed to a kernel.
+static __device__ __align__(256) float scratch[FA_BWD_NOALLOC_MAX_ROWS];
 
 namespace {
 
@@ -94,6 +101,27 @@ int bwd_impl(int dtype, const void* Q, const void* K, const void* V, const void*
   (void)hipGetLastError();
   if ((st = launched(fa::launch_bwd_dot(a, s))) != FA_OK) return st;
   return launched(fa::launch_bwd_grads(a, s));
+}
+
+std::atomic<float*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_address(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_DEVICE;
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* a = nullptr;
+      if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || a == nullptr) return FA_ERR_DEVICE;
+      p = static_cast<float*>(a);
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FA_OK;
 }
 
 // The baseline's extra limits: rows of at most kBaseMaxN keys (its softmax
@@ -210,6 +238,29 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
            float scale, int stabilize, void* stream) {
   return bwd_impl(FA_BF16, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, B, H, N, d, causal, scale,
                   stabilize, stream);
+}
+
+int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
+                   void* dQ, void* dK, void* dV, int B, int H, int N, int d, int causal, float scale, int stabilize,
+                   void* stream) {
+  (void)stabilize;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if ((long double)B * H * N > (long double)FA_BWD_NOALLOC_MAX_ROWS) return FA_ERR_TOO_LARGE;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(dO, 16) ||
+      !aligned(LSE, 4) || !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16))
+    return FA_ERR_INVALID_ARG;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if ((st = check_device()) != FA_OK) return st;
+  float* Dvec = nullptr;
+  if ((st = scratch_address(&Dvec)) != FA_OK) return st;
+  // D is written in full by the row-dot launch before the gradient launch
+  // reads it, so nothing in the scratch needs clearing between calls
+  fa::BwdArgs a{Q, K, V, O, dO, LSE, Dvec, dQ, dK, dV, B, H, N, d, causal != 0, scale, fa::kBF16};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if ((st = launched(fa::launch_bwd_dot(a, s))) != FA_OK) return st;
+  return launched(fa::launch_bwd_grads(a, s));
 }
 
 int fa_fwd_ex(int dtype, const void* Q, const void* K, const void* V, void* O, float* LSE,
@@ -341,6 +392,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_bwd_workspace_bytes()";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_DEVICE: return "current device is not a gfx950 GPU, or a device query failed";
+    case FA_ERR_TOO_LARGE: return "B*H*N exceeds the allocation-free backward's scratch (FA_BWD_NOALLOC_MAX_ROWS)";
     default: return "unknown status";
   }
 }

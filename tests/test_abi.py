@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4, -5, 7):
+    for code in (0, -1, -2, -3, -4, -5, -6, 7):
         assert isinstance(fa.status_string(code), str) and fa.status_string(code)
     assert fa.status_string(0) == "ok"
 
@@ -89,6 +89,21 @@ def test_backward_argument_validation(lib):
     assert lib.fa_bwd_dq(*[GOOD] * 6, GOOD, 1, 1, 8, 64, 1, -1.0, None) == -1
     assert lib.fa_bwd_grads(*[GOOD] * 6, GOOD, P(4100), GOOD, 1, 1, 8, 64, 1, 0.125, None) == -1
     assert lib.fa_bwd_grads(*[GOOD] * 9, 1, 1, 8, 80, 1, 0.125, None) == -2
+
+
+def test_noalloc_backward_validation(lib):
+    """fa_bwd_noalloc refuses a problem past its fixed scratch, and bad
+    arguments, before any device work (here: with no GPU at all)."""
+    n = fa.NOALLOC_MAX_ROWS
+    assert n == 4194304
+    assert lib.fa_bwd_noalloc(*[GOOD] * 9, 1, 1, n + 1, 64, 1, 0.125, 0, None) == -6
+    assert lib.fa_bwd_noalloc(*[GOOD] * 9, 2, 4, n // 8 + 1, 64, 1, 0.125, 0, None) == -6
+    assert lib.fa_bwd_noalloc(None, *[GOOD] * 8, 1, 1, 8, 64, 1, 0.125, 0, None) == -1
+    assert lib.fa_bwd_noalloc(*[GOOD] * 8, P(4098), 1, 1, 8, 64, 1, 0.125, 0, None) == -1
+    assert lib.fa_bwd_noalloc(*[GOOD] * 9, 1, 1, 8, 96, 1, 0.125, 0, None) == -2
+    assert lib.fa_bwd_noalloc(*[GOOD] * 9, 1, 1, 8, 64, 1, float("nan"), 0, None) == -1
+    # a valid call within the limit reaches the device check (no GPU here)
+    assert lib.fa_bwd_noalloc(*[GOOD] * 9, 2, 4, n // 8, 64, 1, 0.125, 0, None) == -5
 
 
 def test_typed_entry_points_validate_dtype_and_arguments(lib):
