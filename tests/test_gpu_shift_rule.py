@@ -135,7 +135,11 @@ def _emulation_agreement(fa, w, heads):
                 s[0] += int((a == e).sum())
                 s[1] += a.size
                 if a.size:
-                    s[2] = max(s[2], float((np.abs(a - e) / Mt.bf16_ulp(e)).max()))
+                    # in ulps of each row's largest |O| (an element near zero after
+                    # cancellation differs by tiny absolute amounts that are many
+                    # ulps of its own size)
+                    scale = Mt.bf16_ulp(np.abs(e).max(axis=-1, keepdims=True))
+                    s[2] = max(s[2], float((np.abs(a - e) / scale).max()))
         out[stab] = acc
     return out
 
@@ -144,8 +148,9 @@ def _emulation_agreement(fa, w, heads):
 def test_shifted_and_unshifted_rows_match_the_emulation(fa, name):
     """The kernel shifts exactly the rows the emulation shifts, and its
     outputs equal the emulation's bit for bit on at least 99% of the elements
-    of each kind of row, within one bf16 ulp elsewhere (MFMA summation order
-    and the hardware exp2 differ from the CPU's)."""
+    of each kind of row, and elsewhere within one bf16 ulp of the row's
+    largest output (MFMA summation order and the hardware exp2 differ from
+    the CPU's)."""
     w = F.WORKLOADS[name]
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     say(f"{name}: emulation agreement on {len(heads)} heads")
