@@ -90,8 +90,8 @@ int fa_fwd_diag(const void* Q, const void* K, const void* V, void* O, float* LSE
 
 /* Forward pass split over keys, for launches too small to fill the GPU (a
  * single head, short sequences).  Each (head, 128-row query block) is cut
- * into `splits` contiguous ranges of its key blocks (fa_fwd_tile: 64 keys at
- * d = 128, 128 at d = 64), one workgroup each.
+ * into `splits` contiguous ranges of its 128-key blocks (fa_fwd_tile), one
+ * workgroup each.
  * A workgroup first replays the key blocks before its range through the
  * running row maximum and repeated-maximum bookkeeping alone (scores only,
  * no exponentials or products), so its own blocks are shifted, and their
@@ -306,9 +306,9 @@ void fa_stabilize_params(float* delta_min, float* delta_max, float* fold);
 int fa_stabilize_params_ex(int dtype, float* delta_min, float* delta_max, float* fold);
 
 /* Tile shape of the forward kernel for head dimension d (reporting only):
- * query rows per workgroup and keys per block (128 and 64 for d = 128; 128
- * and 128 for d = 64); 0 for unsupported d.  The key block is also the unit
- * of the running maximum and repeated-maximum bookkeeping. */
+ * query rows per workgroup and keys per block (128 and 128 for both d = 64
+ * and d = 128); 0 for unsupported d.  The key block is also the unit of the
+ * running maximum and repeated-maximum bookkeeping. */
 void fa_fwd_tile(int d, int* block_q, int* block_k);
 
 /* Library version, major*10000 + minor*100 + patch. */

@@ -224,13 +224,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(
 // Rows [r0, r0 + ROWS) of X (N rows) into a swizzled tile with dma16 (r0 and
 // tile wave-uniform, r0 < N).  Rows past N read row N-1 (in bounds);
 // zero_tail() clears them afterwards.  off[] from tile_offsets().
-template <int D, int ROWS, int NT>
+// FULL: the caller guarantees r0 + ROWS <= N (no branch is emitted).
+template <int D, int ROWS, int NT, bool FULL = false>
 __device__ __forceinline__ void load_tile_async(const int* off, const bf16_t* __restrict__ X, int r0, int N,
                                                 bf16_t* tile, int wave, int lane) {
   constexpr int CPR = D / 8;
   constexpr int PER_LANE = ROWS * CPR / NT;
   const bf16_t* base = X + (size_t)r0 * D;
-  if (r0 + ROWS <= N) {
+  if (FULL || r0 + ROWS <= N) {
     // copy r covers rows r * (NT / CPR) + (the rows of copy 0), and the
     // swizzle repeats every 16 rows: its offsets are copy 0's plus a
     // uniform step, which goes into the scalar base

@@ -13,11 +13,9 @@
 // maximum is strictly below 1 (the rule is in fa_device.hpp).
 //
 // Mapping onto CDNA4.  A workgroup of 4 waves owns 128 query rows, 32 per
-// wave; keys arrive in blocks of 64 (d = 128) or 128 (d = 64).  K and V
-// tiles are copied straight from HBM into swizzled LDS tiles
-// (global_load_lds_dwordx4, no register staging): at d = 128 two blocks ahead
-// for K and one ahead for V, with one barrier per block; at d = 64 one tile
-// of each, K[j+1] landing during block j's softmax and products.
+// wave; keys arrive in blocks of 128.  K and V tiles (one of each) are
+// copied straight from HBM into swizzled LDS tiles (global_load_lds_dwordx4,
+// no register staging).
 // Scores are formed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16: K
 // rows come from LDS as the A operand, the wave's Q rows stay in registers as
 // the B operand, and each lane ends up owning one query row (lanes l and l+32
@@ -25,10 +23,14 @@
 // in-lane work plus one exchange with lane l^32, and the BF16 probabilities
 // are already laid out as the B operand of O^T = V^T P^T: no LDS round trip
 // for P.  V^T is read from the row-major V tile with the gfx950 transposing
-// LDS read.  O^T and l stay in registers until the epilogue.  At d = 128 the
-// scores of block j+1 are issued in the same basic block as the softmax of
-// block j, so the MFMAs of one overlap the VALU/exponential work of the
-// other; at d = 64 that overlap comes from the other waves on the SIMD.
+// LDS read.  O^T and l stay in registers until the epilogue.
+// d = 64 runs the blocks one after the other (V[j] lands during block j's
+// scores, K[j+1] during its softmax and products) at three waves per SIMD,
+// and the other waves on the SIMD supply the overlap.  d = 128 runs two
+// stages per block at two waves per SIMD: the scores of block j+1 beside the
+// rescale of O for block j, then block j's product with V beside the softmax
+// of block j+1, each stage one basic block with its LDS operand reads
+// scheduled a few MFMAs ahead.
 //
 // Workgroups map to (head, query block) in per-XCD head groups, head-major
 // or, for small launches, block-major (see the kernel's first lines).
@@ -48,11 +50,14 @@ struct FwdTile {
   static constexpr int BQ = kFwdBlockQ;      // query rows per workgroup (4 waves x 32)
   static constexpr int BK = fwd_block_k(D);  // keys per block
   static constexpr int TILE = BK * D;        // one swizzled K or V tile (elements)
-  // Sequential blocks (d = 64): one K and one V tile; K[j+1] lands during
-  // block j's softmax and products, V[j] during its scores.  Otherwise two
-  // of each, and the next block's scores overlap this block's softmax.
-  static constexpr bool SEQ = BK == 128;
-  static constexpr int NTILES = SEQ ? 2 : 4;
+  // One K and one V tile at both head sizes.  d = 64, sequential blocks:
+  // K[j+1] lands during block j's softmax and products, V[j] during its
+  // scores, and the other waves on the SIMD supply the overlap.  d = 128,
+  // two stages per block: the scores of block j+1 are formed while O is
+  // rescaled for block j, then block j's product with V runs while the
+  // softmax of block j+1 is computed.
+  static constexpr bool SEQ = D == 64;
+  static constexpr int NTILES = 2;
 };
 
 // Per-wave softmax state of 32 query rows (one row per lane pair).
@@ -72,6 +77,21 @@ struct SplitOut {
   int splits;
 };
 
+// Schedule of one stage: LEAD groups of RD LDS operand reads first, then,
+// per MFMA, the MFMA, the reads of a later one, and VALU instructions --
+// so the operand reads run a few products ahead and the vector work fills
+// the matrix pipe's shadow without holding many operands in flight.
+template <int NMFMA, int RD, int LEAD, int VALU>
+__device__ __forceinline__ void interleave() {
+  __builtin_amdgcn_sched_group_barrier(0x100, RD * LEAD, 0);
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i + LEAD < NMFMA) __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+    if (VALU > 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
+  }
+}
+
 // SPLIT: the workgroup covers one of `splits` contiguous ranges of its key
 // blocks.  It first replays the blocks before its range through the row
 // maximum and repeated-maximum bookkeeping only (scores, no exponentials or
@@ -86,8 +106,7 @@ __global__ __launch_bounds__(256, FwdTile<D>::SEQ ? 3 : 2) void fwd_kernel(
   using T = FwdTile<D>;
   constexpr int NS = T::BK / 32;   // 32-key subtiles per block
   constexpr int NK = T::BK / 16;   // 16-key MFMA steps per block
-  // d = 128: two K tiles and two V tiles (K[j+1] and V[j] are read while
-  // K[j+2] and V[j+1] land); d = 64: one of each (direct global -> LDS loads)
+  // one K tile and one V tile (direct global -> LDS copies)
   __shared__ __attribute__((aligned(16))) bf16_t smem[T::NTILES * T::TILE];
   bf16_t* const Kbuf = smem;
   bf16_t* const Vbuf = smem + (T::NTILES / 2) * T::TILE;
@@ -189,14 +208,22 @@ __global__ __launch_bounds__(256, FwdTile<D>::SEQ ? 3 : 2) void fwd_kernel(
   auto track = [&](const f32x16* s) {
     // block row maximum; stabilised: also the second largest value, two
     // entries at a time: a' = max(a, x, y), b' = max(b, med3(a, x, y))
+    // (four entries per step: a = max(m, x, y), t = med3(m, x, y),
+    // a' = max(a, z, w), t' = med3(a, z, w), b' = max(b, t, t'): five
+    // instructions for four entries)
     float mx = kNegInf, m2 = kNegInf;
 #pragma unroll
     for (int t = 0; t < NS; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const float x = s[t][i], y = s[t][i + 1];
-        if (STAB) m2 = __builtin_fmaxf(m2, __builtin_amdgcn_fmed3f(mx, x, y));
-        mx = __builtin_fmaxf(mx, __builtin_fmaxf(x, y));
+      for (int i = 0; i < 16; i += 4) {
+        const float x = s[t][i], y = s[t][i + 1], z = s[t][i + 2], w = s[t][i + 3];
+        const float a = __builtin_fmaxf(mx, __builtin_fmaxf(x, y));
+        if (STAB) {
+          const float t0 = __builtin_amdgcn_fmed3f(mx, x, y);
+          const float t1 = __builtin_amdgcn_fmed3f(a, z, w);
+          m2 = __builtin_fmaxf(m2, __builtin_fmaxf(t0, t1));
+        }
+        mx = __builtin_fmaxf(a, __builtin_fmaxf(z, w));
       }
     float mx_lo, mx_hi;
     lane_pair(mx, mx_lo, mx_hi);
@@ -225,8 +252,10 @@ __global__ __launch_bounds__(256, FwdTile<D>::SEQ ? 3 : 2) void fwd_kernel(
   };
 
   // Online softmax of one block held in s (masked already): updates the row
-  // state, rescales O, and returns bf16(P) as B operands in pb.
-  auto softmax = [&](f32x16* s, bf16x8* pb) {
+  // state (maximum, tie state, shift, row sum), replaces the scores by the
+  // unnormalised FP32 probabilities, and returns the factor alpha by which O
+  // must be rescaled before this block's product with V.
+  auto online = [&](f32x16* s) {
     const float Mn = track(s);
     const float alpha = exp2_fast(st.M - Mn);  // 0 on the first block (M = -inf)
     st.M = Mn;
@@ -240,14 +269,23 @@ __global__ __launch_bounds__(256, FwdTile<D>::SEQ ? 3 : 2) void fwd_kernel(
         lsum += p;
       }
     st.l = alpha * st.l + lsum;
+    return alpha;
+  };
+  auto rescale = [&](float alpha) {
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+  };
+  // bf16(P) of the block in s, as the B operands of its product with V
+  auto pack = [&](const f32x16* s, bf16x8* pb) {
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) pb[ks] = pack8<E>(s[ks >> 1], (ks & 1) * 8);
   };
-
+  auto softmax = [&](f32x16* s, bf16x8* pb) {
+    rescale(online(s));
+    pack(s, pb);
+  };
   // O^T += V^T bf16(P)^T for one block.
   auto pv = [&](const bf16_t* Vs, const bf16x8* pb) {
     const uint32_t va = (uint32_t)opaque((int)vx0), vb = (uint32_t)opaque((int)vx1);
@@ -272,9 +310,7 @@ __global__ __launch_bounds__(256, FwdTile<D>::SEQ ? 3 : 2) void fwd_kernel(
       }
   };
 
-  // Two score buffers swap roles every block (the loop is unrolled by two),
-  // so the next block's scores need no register copy.
-  f32x16 sa[NS], sb[NS];
+  f32x16 sa[NS];
 
   if (SPLIT) {
     // ---- replay of the blocks before this range: scores and the running
@@ -335,58 +371,107 @@ __global__ __launch_bounds__(256, FwdTile<D>::SEQ ? 3 : 2) void fwd_kernel(
       __syncthreads();  // K[j+1] complete; every wave's reads of V[j] are done
     }
   } else {
-    // ---- prologue: K[jb], V[jb] (and K[jb+1]) into LDS; scores of block jb
+    // ---- two stages per block (d = 128).  With P[j] and alpha[j] from the
+    // softmax of block j, block j runs
+    //   A: S[j+1] = K[j+1] Q^T (MFMA)        with  O *= alpha[j] (VALU)
+    //   B: O += V[j]^T P[j]^T  (MFMA)        with  the softmax of block j+1
+    // so that each stage pairs matrix work with vector work in one basic
+    // block.  P[j+1] overwrites P[j] only after B's products have read it
+    // (one P buffer).  The K tile holds K[j+1] during A and receives K[j+2]
+    // during B; the V tile receives V[j] during A and holds it during B.  The
+    // per-element arithmetic and its order are those of a sequential block:
+    // rescale, then the product.
+    bf16x8 pb[NK];
+    float alpha = 0.0f;
     if (jb < je) {
+      // prologue: the scores and softmax of block jb; K[jb+1] lands meanwhile
       load_tile_async<D, T::BK, 256>(ldoff, Kh, jb * T::BK, N, Kbuf, wave, lane);
-      load_tile_async<D, T::BK, 256>(ldoff, Vh, jb * T::BK, N, Vbuf, wave, lane);
-      if (jb + 1 < je) load_tile_async<D, T::BK, 256>(ldoff, Kh, (jb + 1) * T::BK, N, Kbuf + T::TILE, wave, lane);
       wait_vmem();
-      wait_vmem_tracked();
       zero_tail<D, T::BK, 256>(jb * T::BK, N, Kbuf, wave, lane);
-      zero_tail<D, T::BK, 256>(jb * T::BK, N, Vbuf, wave, lane);
-      if (jb + 1 < je) zero_tail<D, T::BK, 256>((jb + 1) * T::BK, N, Kbuf + T::TILE, wave, lane);
       __syncthreads();
-      if (jb < n_wave) scores(Kbuf, sa);
-      // The first iteration copies block jb+2 into the tile these scores were
-      // just read from; every wave's reads of it must be complete before any
-      // wave issues that copy.
-      if (jb + 2 < je) __syncthreads();
-    }
-    // (On every path into the block loop the compiler must see the prologue's
-    // register loads completed, or it waits for them, and with them for the
-    // loop's tile prefetches, inside the loop.)
-    wait_vmem_tracked();
-
-    auto iteration = [&](int j, f32x16* sc, f32x16* sn) {
-      // Prefetch: K[j+2] into the K tile block j used, V[j+1] into the V tile
-      // block j-1 used; both were released by the barrier that ended j-1.
-      const int jj = j - jb;  // tile slots alternate from the first block of the range
-      bf16_t* const kdst = Kbuf + (jj & 1) * T::TILE;
-      bf16_t* const vdst = Vbuf + ((jj + 1) & 1) * T::TILE;
-      if (j + 2 < je) load_tile_async<D, T::BK, 256>(ldoff, Kh, (j + 2) * T::BK, N, kdst, wave, lane);
-      if (j + 1 < je) load_tile_async<D, T::BK, 256>(ldoff, Vh, (j + 1) * T::BK, N, vdst, wave, lane);
-
-      if (j < n_wave) {
-        const int kb0 = j * T::BK;
-        if ((kb0 + T::BK > N) || (CAUSAL && kb0 + T::BK - 1 > qw0)) mask(sc, kb0);
-        // The scores of the next block are issued together with this block's
-        // softmax: independent work in one basic block, so the MFMAs can
-        // overlap the VALU and exponential instructions.  On the wave's last
-        // block they read a stale (in-bounds) tile and are discarded.
-        bf16x8 pb[NK];
-        scores(Kbuf + ((jj + 1) & 1) * T::TILE, sn);
-        softmax(sc, pb);
-        pv(Vbuf + (jj & 1) * T::TILE, pb);
+      const int kb0 = jb * T::BK;
+      if (jb < n_wave) {
+        scores(Kbuf, sa);
+        if ((kb0 + T::BK > N) || (CAUSAL && kb0 + T::BK - 1 > qw0)) mask(sa, kb0);
+      }
+      __syncthreads();  // every wave's reads of K[jb] are done
+      if (jb + 1 < je) load_tile_async<D, T::BK, 256>(ldoff, Kh, kb0 + T::BK, N, Kbuf, wave, lane);
+      if (jb < n_wave) {
+        alpha = online(sa);
+        pack(sa, pb);
       }
       wait_vmem();
-      if (j + 2 < je) zero_tail<D, T::BK, 256>((j + 2) * T::BK, N, kdst, wave, lane);
-      if (j + 1 < je) zero_tail<D, T::BK, 256>((j + 1) * T::BK, N, vdst, wave, lane);
+      if (jb + 1 < je) zero_tail<D, T::BK, 256>(kb0 + T::BK, N, Kbuf, wave, lane);
+      __syncthreads();  // K[jb+1] complete
+    }
+    // (on every path into the block loop the compiler must see the
+    // prologue's register loads completed, or it waits for them, and with
+    // them for the loop's tile copies, inside the loop)
+    wait_vmem_tracked();
+    // The steady stages (every block but the range's last two or three):
+    // block j+1 is in the range and needs no mask, V[j] and K[j+2] are whole
+    // blocks inside N and K[j+2] is in the range, so each stage is one basic
+    // block with no branch.  The schedule of each stage is pinned (operand
+    // reads a few products ahead of their MFMA), and nothing moves across a
+    // stage boundary: work pulled across would lengthen live ranges past the
+    // register budget.
+    auto steady = [&](int j) {
+      const int kb0 = j * T::BK;
+      const int kn0 = kb0 + T::BK;  // first key of block j+1
+      // ---- A: V[j] into the V tile (its reads of block j-1 ended at the
+      // last barrier); S[j+1] from the K tile; O *= alpha[j]
+      load_tile_async<D, T::BK, 256, true>(ldoff, Vh, kb0, N, Vbuf, wave, lane);
+      scores(Kbuf, sa);
+      rescale(alpha);
+      interleave<NS * D / 16, 1, 4, 0>();
+      wait_vmem();
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();  // V[j] complete; every wave's reads of K[j+1] are done
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- B: K[j+2] into the K tile; O += V[j]^T P[j]^T; softmax of block j+1
+      load_tile_async<D, T::BK, 256, true>(ldoff, Kh, kn0 + T::BK, N, Kbuf, wave, lane);
+      pv(Vbuf, pb);
+      alpha = online(sa);
+      interleave<NK * D / 32, 2, 3, 0>();
+      // P[j+1] replaces P[j] once the products have read it
+      __builtin_amdgcn_sched_barrier(0);
+      pack(sa, pb);
+      wait_vmem();
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();  // K[j+2] complete; every wave's reads of V[j] are done
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // The same two stages for any block, with every condition at run time:
+    // the range's last blocks, and waves past N (copies and barriers only).
+    auto general = [&](int j) {
+      const int kb0 = j * T::BK;
+      const int kn0 = kb0 + T::BK;
+      const bool live = j < n_wave;
+      const bool next = j + 1 < je && j + 1 < n_wave;
+      load_tile_async<D, T::BK, 256>(ldoff, Vh, kb0, N, Vbuf, wave, lane);
+      if (next) scores(Kbuf, sa);
+      if (live) rescale(alpha);
+      wait_vmem();
+      zero_tail<D, T::BK, 256>(kb0, N, Vbuf, wave, lane);
+      __syncthreads();
+      if (j + 2 < je) load_tile_async<D, T::BK, 256>(ldoff, Kh, kn0 + T::BK, N, Kbuf, wave, lane);
+      if (live) pv(Vbuf, pb);
+      if (next) {
+        if ((kn0 + T::BK > N) || (CAUSAL && kn0 + T::BK - 1 > qw0)) mask(sa, kn0);
+        alpha = online(sa);
+        pack(sa, pb);
+      }
+      wait_vmem();
+      if (j + 2 < je) zero_tail<D, T::BK, 256>(kn0 + T::BK, N, Kbuf, wave, lane);
       __syncthreads();
     };
-    for (int j = jb; j < je; j += 2) {
-      iteration(j, sa, sb);
-      if (j + 1 < je) iteration(j + 1, sb, sa);
-    }
+    // With 128-key blocks and 128-row query blocks a live wave computes every
+    // block of the range and only the row's last block can need the mask.
+    static_assert(T::BK == T::BQ, "one causal bound per workgroup");
+    const int j_steady = n_wave >= je ? max(jb, min(je - 2, N / T::BK - 2)) : jb;
+    int j = jb;
+    for (; j < j_steady; ++j) steady(j);
+    for (; j < je; ++j) general(j);
   }
 
   // ---- epilogue: O = O_bar / l (as O_bar * (1/l)), LSE = (M + log2 l) ln 2

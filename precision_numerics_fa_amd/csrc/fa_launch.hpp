@@ -98,9 +98,9 @@ constexpr int kHbmProbeBlocks = 4096;
 hipError_t launch_read_probe(const void* src, uint32_t* sink, long long n16, hipStream_t stream);
 
 constexpr int kFwdBlockQ = 128;
-// Keys per block of the forward: 128 for d = 64 (one K and one V tile, the
-// block's products after its softmax), 64 for d = 128 (two of each, the next
-// block's scores issued with this block's softmax).
-constexpr int fwd_block_k(int d) { return d == 64 ? 128 : 64; }
+// Keys per block of the forward (both head sizes): one K and one V tile of
+// 128 keys; the running maximum and repeated-maximum bookkeeping advance a
+// block at a time.
+constexpr int fwd_block_k(int d) { return d == 64 || d == 128 ? 128 : 0; }
 
 }  // namespace fa
