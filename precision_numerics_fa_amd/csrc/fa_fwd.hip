@@ -77,21 +77,6 @@ struct SplitOut {
   int splits;
 };
 
-// Schedule of one stage: LEAD groups of RD LDS operand reads first, then,
-// per MFMA, the MFMA, the reads of a later one, and VALU instructions --
-// so the operand reads run a few products ahead and the vector work fills
-// the matrix pipe's shadow without holding many operands in flight.
-template <int NMFMA, int RD, int LEAD, int VALU>
-__device__ __forceinline__ void interleave() {
-  __builtin_amdgcn_sched_group_barrier(0x100, RD * LEAD, 0);
-#pragma unroll
-  for (int i = 0; i < NMFMA; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i + LEAD < NMFMA) __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
-    if (VALU > 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
-  }
-}
-
 // SPLIT: the workgroup covers one of `splits` contiguous ranges of its key
 // blocks.  It first replays the blocks before its range through the row
 // maximum and repeated-maximum bookkeeping only (scores, no exponentials or
