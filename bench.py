@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the short timing of the other bf16 workloads after the step")
     ap.add_argument("--cpu-heads", type=int, default=128,
                     help="heads the CPU oracle checks and times (all 128 of the workload by default)")
     ap.add_argument("--sweep", action="store_true",
@@ -282,6 +284,8 @@ def main():
     fa.fwd(q, k, v, causal=True, stabilize=False, out=o_plain, lse=torch.empty_like(lse))
     base = baseline_leg(args, q, k, v, fwd_flop, kern_ms["fwd"])
     out["baseline_fp32acc"] = base.pop("record")
+    if not args.no_other_workloads:
+        out["other_workloads"] = other_workloads_leg()
     if not args.no_cpu_baseline:
         out["tie_bias"] = tie_bias_leg()
         out.update(cpu_baseline_leg(w, full, o, lse, dq, dk, dv, args.cpu_heads, fwd_flop + bwd_flop,
@@ -454,6 +458,44 @@ def _timed(fn, reps):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps
+
+
+def other_workloads_leg(reps: int = 20):
+    """The other bf16 workloads' forward (fix on) and backward, timed with
+    HIP events after the step benchmark: the fastest of three rounds of
+    `reps` calls each (the sweep's method, fewer calls)."""
+    import numpy as np
+    import torch
+
+    import fa_inputs as F
+    import precision_numerics_fa_amd as fa
+
+    recs = {}
+    for name in ("c1", "c2", "c3", "c5"):
+        w = F.WORKLOADS[name].with_shape(with_do=True)
+        B, H, N, d = w.B, w.H, w.N, w.d
+        full = F.full(w)
+        dev = {n: torch.from_numpy(full[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v", "do")}
+        del full
+        q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        fwd = lambda: fa.fwd(q, k, v, causal=w.causal, stabilize=True, out=o, lse=lse)  # noqa: E731
+        bwd = lambda: fa.bwd(q, k, v, o, do, lse, causal=w.causal)  # noqa: E731
+        _timed(fwd, 4 * reps)
+        t_fwd = min(_timed(fwd, reps) for _ in range(3))
+        fwd()
+        t_bwd = min(_timed(bwd, reps) for _ in range(3))
+        pairs = N * (N + 1) / 2 if w.causal else N * N
+        fwd_flop = 4.0 * B * H * pairs * d
+        recs[name] = {"shape": f"{B}x{H}x{N}x{d}" + (" causal" if w.causal else ""),
+                      "fwd_ms": round(t_fwd, 4),
+                      "fwd_pct_peak": round(100 * fwd_flop / (t_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                      "bwd_ms": round(t_bwd, 4),
+                      "bwd_pct_peak": round(100 * 2.5 * fwd_flop / (t_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+        del dev, q, k, v, do, o, lse
+        torch.cuda.empty_cache()
+    return recs
 
 
 def sweep(args):
