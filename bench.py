@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--issue-probe", action="store_true",
+                    help="print the instruction-issue probe's table (fa_issue_probe) and exit")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the short timing of the other bf16 workloads after the step")
     ap.add_argument("--cpu-heads", type=int, default=128,
@@ -142,6 +144,9 @@ def main():
     fa.load()
     if args.sweep:
         sweep(args)
+        return
+    if args.issue_probe:
+        issue_probe_table()
         return
     if args.bias_toy:
         bias_toy(args)
@@ -458,6 +463,31 @@ def _timed(fn, reps):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps
+
+
+def issue_probe_table(blocks: int = 1024, iters: int = 2048):
+    """fa_issue_probe for every kind at one and two waves per SIMD: the time
+    of one loop iteration of a SIMD's waves (the fastest of three launches)."""
+    import torch
+
+    import precision_numerics_fa_amd as fa
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    rows = []
+    for kind, name in enumerate(fa.ISSUE_PROBE_KINDS):
+        rec = {"kind": kind, "work_per_wave_and_iteration": name}
+        for w in (1, 2):
+            if kind == 7 and w == 1:
+                continue
+            fn = lambda: fa.issue_probe(kind, w, blocks, iters, out)  # noqa: E731
+            fn()
+            best = min(_timed(fn, 1) for _ in range(3))
+            rec[f"ns_per_iteration_{w}_wave" + ("s" if w == 2 else "")] = round(
+                best * 1e6 / (blocks / cus) / iters, 2)
+        rows.append(rec)
+        print(json.dumps(rec), flush=True)
+    return rows
 
 
 def other_workloads_leg(reps: int = 20):

@@ -47,6 +47,8 @@ from ._lib import (  # noqa: F401
     fwd_tile,
     lib_path,
     hbm_probe,
+    issue_probe,
+    ISSUE_PROBE_KINDS,
     load,
     mfma_probe,
     stabilize_params,

@@ -37,6 +37,7 @@ _SIGNATURES = {
     "fa_base_pv": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fa_mfma_probe": (ctypes.c_longlong, [_P, _I, _I, _P]),
     "fa_hbm_probe": (_I, [_P, _S, _P, _P]),
+    "fa_issue_probe": (_I, [_I, _I, _P, _I, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_stabilize_params": (None, [ctypes.POINTER(_F)] * 3),
     "fa_stabilize_params_ex": (_I, [_I] + [ctypes.POINTER(_F)] * 3),
@@ -464,6 +465,20 @@ def hbm_probe(src, sink=None):
         raise ValueError(f"sink must hold {HBM_PROBE_THREADS} 32-bit values")
     _call("fa_hbm_probe", _ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream())
     return sink
+
+
+ISSUE_PROBE_KINDS = ("mfma", "v_fma_f32", "v_max3_f32", "v_med3_f32", "v_exp_f32", "v_cvt_pk_bf16_f32",
+                     "mfma+fma", "mfma|fma")
+
+
+def issue_probe(kind: int, waves_per_simd: int, blocks: int = 1024, iters: int = 2048, out=None):
+    """Enqueue the instruction-issue probe (see fa.h); returns out."""
+    torch = _torch()
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda") if out is None else out
+    if out.numel() < blocks * 512 or out.dtype != torch.float32:
+        raise ValueError("out must hold blocks*512 float32 values")
+    _call("fa_issue_probe", int(kind), int(waves_per_simd), _ptr(out), int(blocks), int(iters), _stream())
+    return out
 
 
 # ---------------------------------------------------------------- autograd

@@ -376,6 +376,16 @@ long long fa_mfma_probe(float* out, int blocks, int iters, void* stream) {
   return ls != FA_OK ? ls : fa::mfma_probe_flop(blocks, iters);
 }
 
+int fa_issue_probe(int kind, int waves_per_simd, float* out, int blocks, int iters, void* stream) {
+  if (kind < 0 || kind > 7 || (waves_per_simd != 1 && waves_per_simd != 2) || (kind == 7 && waves_per_simd != 2) ||
+      out == nullptr || !aligned(out, 4) || blocks < 1 || blocks > (1 << 20) || iters < 1)
+    return FA_ERR_INVALID_ARG;
+  const int st = check_device();
+  if (st != FA_OK) return st;
+  (void)hipGetLastError();
+  return launched(fa::launch_issue_probe(kind, 4 * waves_per_simd, out, blocks, iters, static_cast<hipStream_t>(stream)));
+}
+
 int fa_hbm_probe(const void* src, size_t bytes, unsigned int* sink, void* stream) {
   if (!aligned(src, 16) || !aligned(sink, 4) || bytes == 0 || bytes % 16 != 0) return FA_ERR_INVALID_ARG;
   const int st = check_device();

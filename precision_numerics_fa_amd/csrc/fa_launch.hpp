@@ -92,6 +92,7 @@ hipError_t launch_base_pv(const BaseArgs& a, hipStream_t stream);
 // `blocks` workgroups of `iters` iterations, and the launch.
 long long mfma_probe_flop(int blocks, int iters);
 hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t stream);
+hipError_t launch_issue_probe(int kind, int active, float* out, int blocks, int iters, hipStream_t stream);
 // The HBM read-bandwidth probe: reads n16 16-byte units of src; one folded
 // value per thread goes to sink (kHbmProbeBlocks * 256 of them).
 constexpr int kHbmProbeBlocks = 4096;

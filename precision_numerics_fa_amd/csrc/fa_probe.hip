@@ -7,7 +7,8 @@
 // part.  The result is written out so that the chains are not removed.
 // A second probe reads a buffer through HBM (16-byte loads, four in flight
 // per lane) for the read-bandwidth ceiling of the memory-bound kernels, whose
-// traffic is almost all reads.
+// traffic is almost all reads.  A third measures what the instructions of
+// the softmax cost on a SIMD beside MFMA work (issue_probe_kernel).
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -59,6 +60,99 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
   sink[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+// Instruction-issue probe: 512-thread workgroups with 96 KB of LDS, so one
+// per CU and waves w and w + 4 on the same SIMD; waves numbered `active` and
+// up skip the loop (active 4: one wave per SIMD, 8: two).  Per iteration an
+// active wave issues, on registers only:
+//   kind 0: 8 MFMAs on four accumulators
+//   kind 1..5: 64 instructions of one type on eight independent chains:
+//     v_fma_f32, v_max3_f32, v_med3_f32, v_exp_f32, v_cvt_pk_bf16_f32
+//   kind 6: 8 MFMAs, each followed by 8 v_fma_f32
+//   kind 7: waves 0-3 16 MFMAs, waves 4-7 128 v_fma_f32
+// One float per thread goes to out so that nothing is removed.
+template <int KIND>
+__global__ __launch_bounds__(512, 1) void issue_probe_kernel(float* __restrict__ out, int iters, int active) {
+  __shared__ float pad[24576];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  pad[tid] = (float)tid;
+  const float s0 = 1.0f + (float)(tid & 1) * 1e-7f;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(s0 * (float)(i + 1) * (1.0f / 64.0f));
+    b[i] = (__bf16)((s0 - (float)i) * (1.0f / 64.0f));
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = zero16();
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = s0 * 0.01f * (float)(i + 1) + (float)tid * 1e-6f;
+  const float m = 0.999f * s0, c = 1e-3f;
+  // (the work of a wave is decided outside its loop, so the loop has no branch)
+  auto valu_step = [&](int i) {
+    if (KIND == 1 || KIND == 6 || KIND == 7) x[i] = __builtin_fmaf(x[i], m, c);
+    if (KIND == 2) x[i] = __builtin_fmaxf(x[i], __builtin_fmaxf(x[(i + 1) & 7], c));
+    if (KIND == 3) x[i] = __builtin_amdgcn_fmed3f(x[i], x[(i + 1) & 7], c);
+    if (KIND == 4) x[i] = -exp2_fast(x[i]);
+    if (KIND == 5) {  // one v_cvt_pk_bf16_f32, its packed bits fed back as a float
+      typedef __bf16 two_bf16 __attribute__((ext_vector_type(2)));
+      two_bf16 r;
+      r[0] = (__bf16)x[i];
+      r[1] = (__bf16)x[(i + 2) & 7];
+      x[i] = __builtin_bit_cast(float, r);
+    }
+  };
+  if (wave < active) {
+    if (KIND == 0) {
+      for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc[r & 3] = mfma<__bf16>(a, b, acc[r & 3]);
+    } else if (KIND == 6) {
+      for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          acc[r & 3] = mfma<__bf16>(a, b, acc[r & 3]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) valu_step(i);
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+      }
+    } else if (KIND == 7) {
+      if (wave < 4) {
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r & 3] = mfma<__bf16>(a, b, acc[r & 3]);
+      } else {
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) valu_step(i);
+      }
+    } else {
+      for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) valu_step(i);
+    }
+  }
+  float sum = pad[(tid + 1) & 511];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += acc[t][i];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sum += x[i];
+  out[(size_t)blockIdx.x * 512 + tid] = sum;
+}
+
 }  // namespace
 
 hipError_t launch_read_probe(const void* src, uint32_t* sink, long long n16, hipStream_t s) {
@@ -68,6 +162,21 @@ hipError_t launch_read_probe(const void* src, uint32_t* sink, long long n16, hip
 
 long long mfma_probe_flop(int blocks, int iters) {
   return (long long)blocks * 4 * iters * kProbeChains * (2LL * 32 * 32 * 16);
+}
+
+hipError_t launch_issue_probe(int kind, int active, float* out, int blocks, int iters, hipStream_t s) {
+  const dim3 g((unsigned)blocks), t(512);
+  switch (kind) {
+    case 0: hipLaunchKernelGGL(issue_probe_kernel<0>, g, t, 0, s, out, iters, active); break;
+    case 1: hipLaunchKernelGGL(issue_probe_kernel<1>, g, t, 0, s, out, iters, active); break;
+    case 2: hipLaunchKernelGGL(issue_probe_kernel<2>, g, t, 0, s, out, iters, active); break;
+    case 3: hipLaunchKernelGGL(issue_probe_kernel<3>, g, t, 0, s, out, iters, active); break;
+    case 4: hipLaunchKernelGGL(issue_probe_kernel<4>, g, t, 0, s, out, iters, active); break;
+    case 5: hipLaunchKernelGGL(issue_probe_kernel<5>, g, t, 0, s, out, iters, active); break;
+    case 6: hipLaunchKernelGGL(issue_probe_kernel<6>, g, t, 0, s, out, iters, active); break;
+    default: hipLaunchKernelGGL(issue_probe_kernel<7>, g, t, 0, s, out, iters, active); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t s) {

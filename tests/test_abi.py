@@ -175,10 +175,19 @@ def test_probe_argument_validation(lib):
     assert lib.fa_hbm_probe(GOOD, 100, P(1 << 20), None) == -1         # not a multiple of 16
     assert lib.fa_hbm_probe(GOOD, 256, None, None) == -1               # no sink
     assert lib.fa_hbm_probe(P(4100), 256, P(1 << 20), None) == -1      # misaligned
+    assert lib.fa_issue_probe(-1, 1, GOOD, 4, 4, None) == -1           # kind outside 0..7
+    assert lib.fa_issue_probe(8, 1, GOOD, 4, 4, None) == -1
+    assert lib.fa_issue_probe(0, 3, GOOD, 4, 4, None) == -1            # one or two waves per SIMD
+    assert lib.fa_issue_probe(7, 1, GOOD, 4, 4, None) == -1            # kind 7 pairs two waves
+    assert lib.fa_issue_probe(0, 1, None, 4, 4, None) == -1
+    assert lib.fa_issue_probe(0, 1, P(4098), 4, 4, None) == -1         # misaligned
+    assert lib.fa_issue_probe(0, 1, GOOD, 0, 4, None) == -1
+    assert lib.fa_issue_probe(0, 1, GOOD, 4, 0, None) == -1
     import torch
     if not torch.cuda.is_available():
         assert lib.fa_mfma_probe(GOOD, 8, 3, None) == -5
         assert lib.fa_hbm_probe(GOOD, 256, P(1 << 20), None) == -5
+        assert lib.fa_issue_probe(7, 2, GOOD, 4, 4, None) == -5
 
 
 def test_header_is_plain_c_and_links(lib, tmp_path):

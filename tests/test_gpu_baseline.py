@@ -227,6 +227,34 @@ def test_mfma_probe_counts_its_flop_and_computes_the_product(fa):
     assert np.array_equal(got, np.broadcast_to(expect, got.shape))
 
 
+def test_issue_probe_runs_every_kind(fa):
+    """The instruction-issue probe: every kind at one and two waves per SIMD
+    launches and completes.  For the MFMA kind (small exact operands) the
+    output of the active waves grows with the iteration count by the product
+    its operands define, and that of the idle waves does not change: only the
+    requested waves run the loop."""
+    import torch
+    blocks = 8
+    for kind in range(len(fa.ISSUE_PROBE_KINDS)):
+        for w in (1, 2):
+            if kind == 7 and w == 1:
+                continue
+            print(f"issue probe kind {kind} ({fa.ISSUE_PROBE_KINDS[kind]}) waves/SIMD {w}", flush=True)
+            fa.issue_probe(kind, w, blocks, 3)
+            torch.cuda.synchronize()
+    for w in (1, 2):
+        o3 = fa.issue_probe(0, w, blocks, 3).cpu().numpy().astype(np.float64).reshape(blocks, 8, 64)
+        o6 = fa.issue_probe(0, w, blocks, 6).cpu().numpy().astype(np.float64).reshape(blocks, 8, 64)
+        diff = o6 - o3
+        active, idle = diff[:, : 4 * w], diff[:, 4 * w :]
+        # every accumulator entry is sum_k a_k b_k = -0.064453125 (a = (j+1)/64,
+        # b = (1-j)/64 over both k halves); three more iterations of two MFMAs
+        # on each of four accumulators of 16 entries add 6 * 64 of them, up to
+        # the float rounding of each thread's total
+        assert np.allclose(active, 6 * 64 * -0.064453125, atol=1e-2), (w, active.min(), active.max())
+        assert np.all(idle == 0), w
+
+
 def test_hbm_probe_reads_every_word(fa):
     """The read probe folds (xor) each thread's words: the xor over all sink
     values equals the xor of the whole buffer, including a tail shorter than
