@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--issue-probe", action="store_true",
                     help="print the instruction-issue probe's table (fa_issue_probe) and exit")
+    ap.add_argument("--power", action="store_true",
+                    help="print the board power and graphics clock (amd-smi, sampled midway through "
+                         "a few seconds of back-to-back calls) for the c4 forward and backward and for "
+                         "the probe's MFMA, LDS-read and VALU kinds, one JSON line each, and exit")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the short timing of the other bf16 workloads after the step")
     ap.add_argument("--cpu-heads", type=int, default=128,
@@ -147,6 +151,9 @@ def main():
         return
     if args.issue_probe:
         issue_probe_table()
+        return
+    if args.power:
+        power_table()
         return
     if args.bias_toy:
         bias_toy(args)
@@ -485,6 +492,77 @@ def issue_probe_table(blocks: int = 1024, iters: int = 2048):
             best = min(_timed(fn, 1) for _ in range(3))
             rec[f"ns_per_iteration_{w}_wave" + ("s" if w == 2 else "")] = round(
                 best * 1e6 / (blocks / cus) / iters, 2)
+        rows.append(rec)
+        print(json.dumps(rec), flush=True)
+    return rows
+
+
+def _smi_sample():
+    """Board power (W) and the mean graphics clock (MHz) over the XCDs from
+    `amd-smi metric --power --clock`, or None where the tool gives none."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--power", "--clock"], capture_output=True, text=True,
+                           timeout=60)
+    except (OSError, subprocess.TimeoutExpired):
+        return None, None
+    p = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", r.stdout)
+    clk = [float(c) for c in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", r.stdout)]
+    return (float(p.group(1)) if p else None), (round(sum(clk) / len(clk), 1) if clk else None)
+
+
+def power_table(seconds: float = 6.0):
+    """What each kind of work draws: calls queued back to back for `seconds`,
+    power and clock sampled halfway, then the rate from HIP events."""
+    import torch
+
+    import fa_inputs as F
+    import precision_numerics_fa_amd as fa
+
+    w = F.WORKLOADS["c4"].with_shape(with_do=True)
+    B, H, N, d = w.B, w.H, w.N, w.d
+    g = torch.Generator(device="cuda").manual_seed(0)
+    q, k, v, do = (torch.randn(B, H, N, d, device="cuda", generator=g).to(torch.bfloat16) for _ in range(4))
+    scale = d ** -0.5
+    o, lse = fa.fwd(q, k, v, causal=True, scale=scale, stabilize=True)
+    flop_f = 4.0 * B * H * N * N * d / 2
+    blocks, iters = 1024, 4096
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    cases = [
+        ("c4 forward, fix on", lambda: fa.fwd(q, k, v, causal=True, scale=scale, stabilize=True),
+         lambda ms: {"tflops": round(flop_f / ms / 1e9, 1)}),
+        ("c4 backward", lambda: fa.bwd(q, k, v, o, do, lse, causal=True, scale=scale),
+         lambda ms: {"tflops": round(2.5 * flop_f / ms / 1e9, 1)}),
+    ]
+    probe_rate = {
+        0: lambda ms: {"tflops": round(blocks * 8 * iters * 8 * 32768 / ms / 1e9, 1)},
+        9: lambda ms: {"tflops": round(blocks * 8 * iters * 8 * 32768 / ms / 1e9, 1),
+                       "lds_bytes_per_clk_per_cu_at_2400mhz": round(
+                           blocks * 8 * iters * 8 * 1024 / (ms * 1e-3) / cus / 2.4e9, 1)},
+        8: lambda ms: {"lds_bytes_per_clk_per_cu_at_2400mhz": round(
+            blocks * 8 * iters * 8 * 1024 / (ms * 1e-3) / cus / 2.4e9, 1)},
+        1: lambda ms: {"ns_per_iteration": round(ms * 1e6 / (blocks / cus) / iters, 1)},
+        4: lambda ms: {"ns_per_iteration": round(ms * 1e6 / (blocks / cus) / iters, 1)},
+    }
+    for kind in (0, 8, 9, 1, 4):
+        cases.append((f"probe: {fa.ISSUE_PROBE_KINDS[kind]}, two waves per SIMD",
+                      (lambda kk: lambda: fa.issue_probe(kk, 2, blocks, iters, out))(kind), probe_rate[kind]))
+    rows = []
+    for name, fn, rate in cases:
+        ms = min(_timed(fn, 3) for _ in range(2))
+        n = max(1, math.ceil(seconds * 1e3 / ms))
+        t0 = time.time()
+        for _ in range(n):
+            fn()
+        while time.time() - t0 < seconds / 2:
+            time.sleep(0.05)
+        watts, mhz = _smi_sample()
+        torch.cuda.synchronize()
+        rec = {"power_probe": name, "socket_power_w": watts, "gfx_clock_mhz": mhz, "ms_per_call": round(ms, 4),
+               "calls_queued": n}
+        rec.update(rate(ms))
         rows.append(rec)
         print(json.dumps(rec), flush=True)
     return rows

@@ -291,18 +291,21 @@ long long fa_mfma_probe(float* out, int blocks, int iters, void* stream);
 int fa_hbm_probe(const void* src, size_t bytes, unsigned int* sink, void* stream);
 
 /* Instruction-issue probe (reporting only): what the softmax's instructions
- * cost on a SIMD beside MFMA work, on registers only.  Launches `blocks`
+ * cost on a SIMD beside MFMA work, and what LDS operand reads add; run
+ * long, it also shows the board power each kind of work draws.  Launches `blocks`
  * workgroups of 512 threads, one per CU (their LDS allocation allows no
  * second), in which `waves_per_simd` (1 or 2) waves per SIMD loop `iters`
  * times; per iteration an active wave issues
  *   kind 0: 8 bf16 MFMAs;  kind 1..5: 64 of v_fma_f32, v_max3_f32,
  *   v_med3_f32, v_exp_f32 or v_cvt_pk_bf16_f32;  kind 6: 8 MFMAs each
  *   followed by 8 v_fma_f32;  kind 7 (two waves per SIMD only): 16 MFMAs in
- *   one wave, 128 v_fma_f32 in the other.
+ *   one wave, 128 v_fma_f32 in the other;  kind 8: 8 LDS reads of 16 bytes
+ *   per lane (ds_read_b128);  kind 9: 8 MFMAs, each with its A operand read
+ *   from LDS (16 bytes per lane).
  * Writes one float per thread to `out` (blocks*512 floats, device memory).
  * Timed with events on `stream`, time / (blocks / CUs) / iters is the time of
  * one iteration of a SIMD's waves.  Returns FA_OK, FA_ERR_INVALID_ARG (kind
- * outside 0..7, waves_per_simd not 1 or 2, kind 7 with one wave, NULL or
+ * outside 0..9, waves_per_simd not 1 or 2, kind 7 with one wave, NULL or
  * misaligned out, non-positive sizes), FA_ERR_DEVICE or FA_ERR_LAUNCH. */
 int fa_issue_probe(int kind, int waves_per_simd, float* out, int blocks, int iters, void* stream);
 

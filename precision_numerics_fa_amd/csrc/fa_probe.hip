@@ -8,7 +8,8 @@
 // A second probe reads a buffer through HBM (16-byte loads, four in flight
 // per lane) for the read-bandwidth ceiling of the memory-bound kernels, whose
 // traffic is almost all reads.  A third measures what the instructions of
-// the softmax cost on a SIMD beside MFMA work (issue_probe_kernel).
+// the softmax cost on a SIMD beside MFMA work, and what LDS operand reads
+// add (issue_probe_kernel).
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -72,10 +73,21 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
 // One float per thread goes to out so that nothing is removed.
 template <int KIND>
 __global__ __launch_bounds__(512, 1) void issue_probe_kernel(float* __restrict__ out, int iters, int active) {
-  __shared__ float pad[24576];
+  __shared__ __attribute__((aligned(16))) float pad[24576];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  pad[tid] = (float)tid;
+  // the first 64 KB hold small bf16 values: the LDS kinds read 16-byte chunks
+  // of it (chunk index below 4096)
+  for (int i = tid; i < 16384; i += 512) {
+    typedef __bf16 two_bf16 __attribute__((ext_vector_type(2)));
+    two_bf16 v;
+    v[0] = (__bf16)((float)(i & 63) * (1.0f / 256.0f));
+    v[1] = (__bf16)((float)(i & 31) * (-1.0f / 256.0f));
+    pad[i] = __builtin_bit_cast(float, v);
+  }
+  __syncthreads();
+  const bf16x8* chunks = reinterpret_cast<const bf16x8*>(pad);
+  uint32_t xr = 0;
   const float s0 = 1.0f + (float)(tid & 1) * 1e-7f;
   bf16x8 a, b;
 #pragma unroll
@@ -123,6 +135,20 @@ __global__ __launch_bounds__(512, 1) void issue_probe_kernel(float* __restrict__
           __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
         }
       }
+    } else if (KIND == 8) {
+      // LDS reads only: 8 ds_read_b128 (1 KB per wave each), folded by XOR
+      for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const uint4 u = __builtin_bit_cast(uint4, chunks[(tid + r * 512 + it * 67) & 4095]);
+          xr ^= u.x ^ u.y ^ u.z ^ u.w;
+        }
+    } else if (KIND == 9) {
+      // 8 MFMAs, each with its A operand read from LDS (1 KB per wave)
+      for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          acc[r & 3] = mfma<__bf16>(chunks[(tid + r * 512 + it * 67) & 4095], b, acc[r & 3]);
     } else if (KIND == 7) {
       if (wave < 4) {
         for (int it = 0; it < iters; ++it)
@@ -150,6 +176,7 @@ __global__ __launch_bounds__(512, 1) void issue_probe_kernel(float* __restrict__
     for (int i = 0; i < 16; ++i) sum += acc[t][i];
 #pragma unroll
   for (int i = 0; i < 8; ++i) sum += x[i];
+  sum += (float)(xr & 255u);
   out[(size_t)blockIdx.x * 512 + tid] = sum;
 }
 
@@ -174,7 +201,9 @@ hipError_t launch_issue_probe(int kind, int active, float* out, int blocks, int 
     case 4: hipLaunchKernelGGL(issue_probe_kernel<4>, g, t, 0, s, out, iters, active); break;
     case 5: hipLaunchKernelGGL(issue_probe_kernel<5>, g, t, 0, s, out, iters, active); break;
     case 6: hipLaunchKernelGGL(issue_probe_kernel<6>, g, t, 0, s, out, iters, active); break;
-    default: hipLaunchKernelGGL(issue_probe_kernel<7>, g, t, 0, s, out, iters, active); break;
+    case 7: hipLaunchKernelGGL(issue_probe_kernel<7>, g, t, 0, s, out, iters, active); break;
+    case 8: hipLaunchKernelGGL(issue_probe_kernel<8>, g, t, 0, s, out, iters, active); break;
+    default: hipLaunchKernelGGL(issue_probe_kernel<9>, g, t, 0, s, out, iters, active); break;
   }
   return hipGetLastError();
 }

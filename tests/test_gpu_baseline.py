@@ -232,7 +232,8 @@ def test_issue_probe_runs_every_kind(fa):
     launches and completes.  For the MFMA kind (small exact operands) the
     output of the active waves grows with the iteration count by the product
     its operands define, and that of the idle waves does not change: only the
-    requested waves run the loop."""
+    requested waves run the loop.  The LDS-read kind adds the fold of the
+    chunks it read, computed here from the values the kernel stores."""
     import torch
     blocks = 8
     for kind in range(len(fa.ISSUE_PROBE_KINDS)):
@@ -253,6 +254,28 @@ def test_issue_probe_runs_every_kind(fa):
         # the float rounding of each thread's total
         assert np.allclose(active, 6 * 64 * -0.064453125, atol=1e-2), (w, active.min(), active.max())
         assert np.all(idle == 0), w
+    # the LDS-read kind folds (xor) the 16-byte chunks it reads; the chunks
+    # hold the bf16 pairs ((i mod 64) / 256, -(i mod 32) / 256) for 32-bit word
+    # i, and iteration `it` of thread t reads chunks (t + 512 r + 67 it) mod
+    # 4096, r < 8; the low byte of the fold is added to the output
+    i = np.arange(16384)
+    bits = lambda x: (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint32)  # noqa: E731
+    words = (bits(-(i % 32) / 256.0) << 16) | bits((i % 64) / 256.0)
+    chunk = np.bitwise_xor.reduce(words.reshape(4096, 4), axis=1)
+    tid = np.arange(512)
+
+    def fold(iters):
+        xr = np.zeros(512, dtype=np.uint32)
+        for it in range(iters):
+            for r in range(8):
+                xr ^= chunk[(tid + 512 * r + 67 * it) & 4095]
+        return (xr & 255).astype(np.float64)
+
+    for w in (1, 2):
+        o3 = fa.issue_probe(8, w, blocks, 3).cpu().numpy().astype(np.float64).reshape(blocks, 512)
+        o6 = fa.issue_probe(8, w, blocks, 6).cpu().numpy().astype(np.float64).reshape(blocks, 512)
+        expect = np.where(tid < 256 * w, fold(6) - fold(3), 0.0)
+        assert np.allclose(o6 - o3, np.broadcast_to(expect, o6.shape), atol=1e-3), w
 
 
 def test_hbm_probe_reads_every_word(fa):
