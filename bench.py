@@ -543,10 +543,15 @@ def power_table(seconds: float = 6.0):
                            blocks * 8 * iters * 8 * 1024 / (ms * 1e-3) / cus / 2.4e9, 1)},
         8: lambda ms: {"lds_bytes_per_clk_per_cu_at_2400mhz": round(
             blocks * 8 * iters * 8 * 1024 / (ms * 1e-3) / cus / 2.4e9, 1)},
+        10: lambda ms: {"lds_bytes_per_clk_per_cu_at_2400mhz": round(
+            blocks * 8 * iters * 16 * 512 / (ms * 1e-3) / cus / 2.4e9, 1)},
+        11: lambda ms: {"tflops": round(blocks * 8 * iters * 8 * 32768 / ms / 1e9, 1),
+                        "lds_bytes_per_clk_per_cu_at_2400mhz": round(
+                            blocks * 8 * iters * 8 * 1024 / (ms * 1e-3) / cus / 2.4e9, 1)},
         1: lambda ms: {"ns_per_iteration": round(ms * 1e6 / (blocks / cus) / iters, 1)},
         4: lambda ms: {"ns_per_iteration": round(ms * 1e6 / (blocks / cus) / iters, 1)},
     }
-    for kind in (0, 8, 9, 1, 4):
+    for kind in (0, 8, 9, 10, 11, 1, 4):
         cases.append((f"probe: {fa.ISSUE_PROBE_KINDS[kind]}, two waves per SIMD",
                       (lambda kk: lambda: fa.issue_probe(kk, 2, blocks, iters, out))(kind), probe_rate[kind]))
     rows = []

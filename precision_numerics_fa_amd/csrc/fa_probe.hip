@@ -149,6 +149,27 @@ __global__ __launch_bounds__(512, 1) void issue_probe_kernel(float* __restrict__
 #pragma unroll
         for (int r = 0; r < 8; ++r)
           acc[r & 3] = mfma<__bf16>(chunks[(tid + r * 512 + it * 67) & 4095], b, acc[r & 3]);
+    } else if (KIND == 10) {
+      // transposing LDS reads only: 16 ds_read_b64_tr_b16 (512 B per wave each)
+      for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const s16x4 u = lds_load_tr4(reinterpret_cast<const bf16_t*>(
+              reinterpret_cast<const char*>(pad) + ((tid * 8 + r * 4096 + it * 536) & 65535)));
+          xr ^= (uint32_t)(uint16_t)u[0] ^ ((uint32_t)(uint16_t)u[1] << 16) ^ (uint32_t)(uint16_t)u[2] ^
+                ((uint32_t)(uint16_t)u[3] << 16);
+        }
+    } else if (KIND == 11) {
+      // 8 MFMAs, each with its A operand from two transposing LDS reads (1 KB)
+      for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const char* base = reinterpret_cast<const char*>(pad);
+          const s16x4 lo = lds_load_tr4(reinterpret_cast<const bf16_t*>(base + ((tid * 8 + r * 8192 + it * 536) & 65535)));
+          const s16x4 hi = lds_load_tr4(
+              reinterpret_cast<const bf16_t*>(base + ((tid * 8 + r * 8192 + 4096 + it * 536) & 65535)));
+          acc[r & 3] = mfma<__bf16>(join8(lo, hi), b, acc[r & 3]);
+        }
     } else if (KIND == 7) {
       if (wave < 4) {
         for (int it = 0; it < iters; ++it)
@@ -203,7 +224,9 @@ hipError_t launch_issue_probe(int kind, int active, float* out, int blocks, int 
     case 6: hipLaunchKernelGGL(issue_probe_kernel<6>, g, t, 0, s, out, iters, active); break;
     case 7: hipLaunchKernelGGL(issue_probe_kernel<7>, g, t, 0, s, out, iters, active); break;
     case 8: hipLaunchKernelGGL(issue_probe_kernel<8>, g, t, 0, s, out, iters, active); break;
-    default: hipLaunchKernelGGL(issue_probe_kernel<9>, g, t, 0, s, out, iters, active); break;
+    case 9: hipLaunchKernelGGL(issue_probe_kernel<9>, g, t, 0, s, out, iters, active); break;
+    case 10: hipLaunchKernelGGL(issue_probe_kernel<10>, g, t, 0, s, out, iters, active); break;
+    default: hipLaunchKernelGGL(issue_probe_kernel<11>, g, t, 0, s, out, iters, active); break;
   }
   return hipGetLastError();
 }
