@@ -481,9 +481,15 @@ __global__ __launch_bounds__(256, FwdTile<D>::SEQ ? 3 : 2) void fwd_kernel(
     }
     return;
   }
-  if (wave_live && myq < N) {
+  // O goes out through LDS (the tiles are idle after the block loop's last
+  // barrier): a lane holds 8-byte pieces of one row, so storing them directly
+  // would write 32 rows in 16-byte pieces per instruction; staged in a
+  // row-major LDS copy of the wave's 32 rows (rows padded by 16 bytes), each
+  // store writes 4 whole rows.
+  if (wave_live) {
+    constexpr int RS = D + 8;  // staged row stride (elements)
+    bf16_t* const stage = smem + wave * 32 * RS;
     const float rinv = 1.0f / lt;
-    bf16_t* Orow = O + hoff + (size_t)myq * D;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
@@ -491,8 +497,18 @@ __global__ __launch_bounds__(256, FwdTile<D>::SEQ ? 3 : 2) void fwd_kernel(
         uint2 w;
         w.x = pack2<E>(o[t][4 * g + 0] * rinv, o[t][4 * g + 1] * rinv);
         w.y = pack2<E>(o[t][4 * g + 2] * rinv, o[t][4 * g + 3] * rinv);
-        *reinterpret_cast<uint2*>(Orow + t * 32 + g * 8 + 4 * hi) = w;
+        *reinterpret_cast<uint2*>(stage + l32 * RS + t * 32 + g * 8 + 4 * hi) = w;
       }
+    constexpr int LPR = D / 8;  // lanes per row (16 bytes each)
+#pragma unroll
+    for (int r0 = 0; r0 < 32; r0 += 64 / LPR) {
+      const int r = r0 + lane / LPR, c = (lane % LPR) * 8;
+      if (qw0 + r < N)
+        *reinterpret_cast<uint4*>(O + hoff + (size_t)(qw0 + r) * D + c) =
+            *reinterpret_cast<const uint4*>(stage + r * RS + c);
+    }
+  }
+  if (wave_live && myq < N) {
     if (hi == 0) {
       LSE[(size_t)bh * N + myq] = (st.M + __builtin_log2f(lt)) * kLn2;
       if (DIAG) row_shifted[(size_t)bh * N + myq] = st.ever ? 1 : 0;
