@@ -80,10 +80,18 @@ __device__ __forceinline__ void load_rows_as_b(bf16x8* f, const bf16_t* rowp, bo
   }
 }
 
-// Write a transposed 32x32 accumulator set (rows = d, lane = one output row)
-// as bf16: element i of subtile t is column d = 32 t + 8 (i/4) + 4 hi + i%4.
+// A wave's 32 output rows, one per lane (lane l32 holds row l32): accumulator
+// set t holds columns 32 t .. 32 t + 31, entry i of it column 32 t + 8 (i/4) +
+// 4 hi + i%4 -- written as bf16 through a row-major LDS copy, rows padded by
+// 16 bytes: stored directly, each instruction would write 32 rows in 16-byte
+// pieces; this way each writes 4 (d = 128) or 8 (d = 64) whole rows.
+// `stage` is 32 * (D + 8) idle elements of LDS owned by the wave; rows at
+// and past `nrows` are not written.
 template <typename E, int D>
-__device__ __forceinline__ void store_row(bf16_t* rowp, const f32x16* acc, float mul, int hi) {
+__device__ __forceinline__ void store_rows_staged(bf16_t* out0, int nrows, const f32x16* acc, float mul, int lane,
+                                                  bf16_t* stage) {
+  constexpr int RS = D + 8;
+  const int l32 = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
 #pragma unroll
@@ -91,8 +99,15 @@ __device__ __forceinline__ void store_row(bf16_t* rowp, const f32x16* acc, float
       uint2 w;
       w.x = pack2<E>(acc[t][4 * g + 0] * mul, acc[t][4 * g + 1] * mul);
       w.y = pack2<E>(acc[t][4 * g + 2] * mul, acc[t][4 * g + 3] * mul);
-      *reinterpret_cast<uint2*>(rowp + t * 32 + g * 8 + 4 * hi) = w;
+      *reinterpret_cast<uint2*>(stage + l32 * RS + t * 32 + g * 8 + 4 * hi) = w;
     }
+  constexpr int LPR = D / 8;  // lanes per row, 16 bytes each
+#pragma unroll
+  for (int r0 = 0; r0 < 32; r0 += 64 / LPR) {
+    const int r = r0 + lane / LPR, c = (lane % LPR) * 8;
+    if (r < nrows)
+      *reinterpret_cast<uint4*>(out0 + (size_t)r * D + c) = *reinterpret_cast<const uint4*>(stage + r * RS + c);
+  }
 }
 
 // Reads of a swizzled tile: the row-major operand read (row sub*32 + l32,
@@ -146,6 +161,7 @@ struct DkdvTile {
   static constexpr int KTILE_BYTES = B32 * D * 2;
   static constexpr int STAGE_BYTES = 2 * 2 * TILE * 2;     // two stages of (Q, dO)
   static constexpr int LDS_BYTES = KTILE_BYTES + STAGE_BYTES + 2 * 2 * BS * 4;
+  static_assert(4 * 32 * (D + 8) * 2 <= LDS_BYTES, "output staging fits the tiles");
 };
 
 // ---------------------------------------------------------------- dK, dV
@@ -311,15 +327,19 @@ __device__ __forceinline__ void dkdv_wg(const bf16_t* __restrict__ Q, const bf16
   for (; qb < qb_plain; ++qb) step(qb, std::true_type{});
   for (; qb <= qb_last; ++qb) step(qb, std::false_type{});
 
-  if (wave_live && myk < N) {
-    store_row<E, D>(dK + hoff + (size_t)myk * D, dk, scale, hi);
-    store_row<E, D>(dV + hoff + (size_t)myk * D, dv, 1.0f, hi);
+  // (the tiles are idle after the loop's last barrier)
+  if (wave_live) {
+    bf16_t* const stage = reinterpret_cast<bf16_t*>(lds) + wave * 32 * (D + 8);
+    const int nrows = min(32, N - kw0);
+    store_rows_staged<E, D>(dK + hoff + (size_t)kw0 * D, nrows, dk, scale, lane, stage);
+    store_rows_staged<E, D>(dV + hoff + (size_t)kw0 * D, nrows, dv, 1.0f, lane, stage);
   }
 }
 
 // dQ kernel tiling: swizzled tiles loaded straight into LDS.
 template <int D>
 struct DqTile {
+  static_assert(4 * 32 * (D + 8) * 2 <= 4 * 64 * D * 2, "output staging fits the tiles");
   static constexpr int B32 = 128;          // queries per workgroup: 4 waves x 32
   static constexpr int BS = 64;            // keys per block (two 32-key subtiles)
   static constexpr int TILE = BS * D;      // one swizzled tile (elements)
@@ -452,7 +472,10 @@ __device__ __forceinline__ void dq_wg(const bf16_t* __restrict__ Q, const bf16_t
   for (; j < n_plain; ++j) step(j, std::false_type{});
   for (; j < n_kblk; ++j) step(j, std::true_type{});
 
-  if (wave_live && myq < N) store_row<E, D>(dQ + hoff + (size_t)myq * D, dq, scale, hi);
+  // (the tiles are idle after the loop's last barrier)
+  if (wave_live)
+    store_rows_staged<E, D>(dQ + hoff + (size_t)qw0 * D, min(32, N - qw0), dq, scale, lane,
+                            smem + wave * 32 * (D + 8));
 }
 
 // Workgroup index -> work item: the hardware hands workgroup i to XCD i % 8;
