@@ -142,15 +142,6 @@ __global__ __launch_bounds__(256, FwdTile<D>::SEQ ? 3 : 2) void fwd_kernel(
 
   // Q rows of this wave as B operands: element j of step kk is d = 16 kk + 8 hi + j.
   bf16x8 qf[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    if (myq < N) {
-      qf[kk] = *reinterpret_cast<const bf16x8*>(Q + hoff + (size_t)myq * D + kk * 16 + hi * 8);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qf[kk][j] = (__bf16)0.0f;
-    }
-  }
 
   // LDS byte offsets of the operand reads at step 0.  The K operand of step
   // kk (row t*32 + l32, chunk 2 kk + hi) sits at offset ^ (kk << 5), and the
@@ -165,6 +156,27 @@ __global__ __launch_bounds__(256, FwdTile<D>::SEQ ? 3 : 2) void fwd_kernel(
 
   int ldoff[T::BK * D / 8 / 256];
   tile_offsets<D, T::BK, 256>(ldoff, wave, lane);
+
+  // The workgroup's Q rows are copied in whole rows into the V tile (idle
+  // until the first block's V), with the first K block into the K tile
+  // (unless a split-key replay needs the K tile first), and each wave reads
+  // its operands from there: loading them straight into registers would
+  // fetch 32 rows in 32-byte pieces per instruction.  Rows past N are zero.
+  static_assert(T::BQ == T::BK, "the Q rows fill one tile");
+  const bool k_first = jb < je && (!SPLIT || jb == 0);
+  load_tile_async<D, T::BQ, 256>(ldoff, Q + hoff, q0, N, Vbuf, wave, lane);
+  if (k_first) load_tile_async<D, T::BK, 256>(ldoff, Kh, jb * T::BK, N, Kbuf, wave, lane);
+  wait_vmem();
+  zero_tail<D, T::BQ, 256>(q0, N, Vbuf, wave, lane);
+  if (k_first) zero_tail<D, T::BK, 256>(jb * T::BK, N, Kbuf, wave, lane);
+  __syncthreads();
+  {
+    const char* qbase = reinterpret_cast<const char*>(Vbuf + wave * 32 * D);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qf[kk] = lds_load8(reinterpret_cast<const bf16_t*>(qbase + (kx0 ^ (uint32_t)(kk << 5))));
+  }
+  __syncthreads();  // every wave holds its Q rows: the V tile may take V
 
   RowState st{kNegInf, kNegInf, 0.0f, false, false};
   f32x16 o[D / 32];
@@ -318,7 +330,7 @@ __global__ __launch_bounds__(256, FwdTile<D>::SEQ ? 3 : 2) void fwd_kernel(
 
   if constexpr (T::SEQ) {
     // ---- sequential blocks: K[j] is in LDS when block j starts
-    if (jb < je) {
+    if (jb < je && !k_first) {
       load_tile_async<D, T::BK, 256>(ldoff, Kh, jb * T::BK, N, Kbuf, wave, lane);
       wait_vmem();
       zero_tail<D, T::BK, 256>(jb * T::BK, N, Kbuf, wave, lane);
@@ -370,10 +382,12 @@ __global__ __launch_bounds__(256, FwdTile<D>::SEQ ? 3 : 2) void fwd_kernel(
     float alpha = 0.0f;
     if (jb < je) {
       // prologue: the scores and softmax of block jb; K[jb+1] lands meanwhile
-      load_tile_async<D, T::BK, 256>(ldoff, Kh, jb * T::BK, N, Kbuf, wave, lane);
-      wait_vmem();
-      zero_tail<D, T::BK, 256>(jb * T::BK, N, Kbuf, wave, lane);
-      __syncthreads();
+      if (!k_first) {
+        load_tile_async<D, T::BK, 256>(ldoff, Kh, jb * T::BK, N, Kbuf, wave, lane);
+        wait_vmem();
+        zero_tail<D, T::BK, 256>(jb * T::BK, N, Kbuf, wave, lane);
+        __syncthreads();
+      }
       const int kb0 = jb * T::BK;
       if (jb < n_wave) {
         scores(Kbuf, sa);
