@@ -499,7 +499,7 @@ __global__ __launch_bounds__(256, FwdTile<D>::SEQ ? 3 : 2) void fwd_kernel(
   // barrier): a lane holds 8-byte pieces of one row, so storing them directly
   // would write 32 rows in 16-byte pieces per instruction; staged in a
   // row-major LDS copy of the wave's 32 rows (rows padded by 16 bytes), each
-  // store writes 4 whole rows.
+  // store writes 4 (d = 128) or 8 (d = 64) whole rows.
   if (wave_live) {
     constexpr int RS = D + 8;  // staged row stride (elements)
     bf16_t* const stage = smem + wave * 32 * RS;
