@@ -573,10 +573,42 @@ def power_table(seconds: float = 6.0):
     return rows
 
 
+def _graph_timed(fn, reps):
+    """GPU time of one call of `fn`: `reps` calls captured in one HIP graph,
+    the fastest of three replays.  Small launches otherwise measure the
+    host's launch rate rather than the kernels."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / reps)
+    del g
+    return best
+
+
 def other_workloads_leg(reps: int = 20):
-    """The other bf16 workloads' forward (fix on) and backward, timed with
-    HIP events after the step benchmark: the fastest of three rounds of
-    `reps` calls each (the sweep's method, fewer calls)."""
+    """The other bf16 workloads' forward (fix on) and backward (row-dot
+    pre-pass and dQ/dK/dV launch, outputs preallocated), each as `reps`
+    calls captured in a HIP graph and replayed (the fastest of three replays):
+    the GPU time per call, without the host's launch overhead, which
+    otherwise dominates the small workloads."""
     import numpy as np
     import torch
 
@@ -593,12 +625,17 @@ def other_workloads_leg(reps: int = 20):
         q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
         o = torch.empty_like(q)
         lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        dvec = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
         fwd = lambda: fa.fwd(q, k, v, causal=w.causal, stabilize=True, out=o, lse=lse)  # noqa: E731
-        bwd = lambda: fa.bwd(q, k, v, o, do, lse, causal=w.causal)  # noqa: E731
-        _timed(fwd, 4 * reps)
-        t_fwd = min(_timed(fwd, reps) for _ in range(3))
+
+        def bwd():
+            fa.bwd_dot(o, do, dvec)
+            fa.bwd_grads(q, k, v, do, lse, dvec, causal=w.causal, dq=dq, dk=dk, dv=dv)
+        _timed(fwd, 4 * reps)  # clocks up
+        t_fwd = _graph_timed(fwd, reps)
         fwd()
-        t_bwd = min(_timed(bwd, reps) for _ in range(3))
+        t_bwd = _graph_timed(bwd, reps)
         pairs = N * (N + 1) / 2 if w.causal else N * N
         fwd_flop = 4.0 * B * H * pairs * d
         recs[name] = {"shape": f"{B}x{H}x{N}x{d}" + (" causal" if w.causal else ""),
@@ -606,7 +643,7 @@ def other_workloads_leg(reps: int = 20):
                       "fwd_pct_peak": round(100 * fwd_flop / (t_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
                       "bwd_ms": round(t_bwd, 4),
                       "bwd_pct_peak": round(100 * 2.5 * fwd_flop / (t_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
-        del dev, q, k, v, do, o, lse
+        del dev, q, k, v, do, o, lse, dvec, dq, dk, dv
         torch.cuda.empty_cache()
     return recs
 
@@ -615,7 +652,8 @@ def sweep(args):
     """Forward (fix on, fix off) and backward throughput on every workload,
     algorithmic FLOP and bytes as in the step benchmark; for the bf16
     workloads also the split-key forward (2, 4 and 8 key ranges, fix on) and
-    the FP32-accumulating baseline."""
+    the FP32-accumulating baseline.  Every figure is the GPU time of one call:
+    `--steps` calls captured in a HIP graph, the fastest of three replays."""
     import numpy as np
     import torch
 
@@ -640,16 +678,21 @@ def sweep(args):
             o = torch.empty_like(q)
             lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
             res.update(o=o, l=lse)
+            dvec = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+            grads = [torch.empty_like(q) for _ in range(3)]
             fon = lambda: fa.fwd(q, k, v, causal=w.causal, stabilize=True, out=o, lse=lse)
             foff = lambda: fa.fwd(q, k, v, causal=w.causal, stabilize=False, out=o, lse=lse)
-            bwd = lambda: fa.bwd(q, k, v, o, do, lse, causal=w.causal)
+
+            def bwd():
+                fa.bwd_dot(o, do, dvec)
+                fa.bwd_grads(q, k, v, do, lse, dvec, causal=w.causal, dq=grads[0], dk=grads[1], dv=grads[2])
         _timed(fon, 4 * reps)  # clocks up
-        # fix on and off alternate; the fastest of three rounds each
-        t_on = min(_timed(fon, reps) for _ in range(3))
-        t_off = min(_timed(foff, reps) for _ in range(3))
-        t_on = min(t_on, *(_timed(fon, reps) for _ in range(2)))
+        # fix on and off alternate; each a graph of `reps` calls, fastest replay
+        t_on = _graph_timed(fon, reps)
+        t_off = _graph_timed(foff, reps)
+        t_on = min(t_on, _graph_timed(fon, reps))
         fon()
-        t_bwd = min(_timed(bwd, reps) for _ in range(3))
+        t_bwd = _graph_timed(bwd, reps)
         t_split = {}
         if w.dtype == "bf16":
             ws_s = torch.empty(fa.fwd_split_workspace_bytes(B, H, N, d, 8), dtype=torch.uint8, device="cuda")
@@ -658,13 +701,13 @@ def sweep(args):
             for ns in (2, 4, 8):
                 fn = lambda ns=ns: fa.fwd_split(q, k, v, ns, causal=w.causal, stabilize=True,  # noqa: E731
                                                 workspace=ws_s, out=o_s, lse=l_s)
-                t_split[ns] = min(_timed(fn, reps) for _ in range(2))
+                t_split[ns] = _graph_timed(fn, reps)
             del ws_s, o_s, l_s
         t_base = None
         if w.dtype == "bf16":
             ws = torch.empty(fa.base_workspace_bytes(B, H, N, d, w.causal), dtype=torch.uint8, device="cuda")
             base = lambda: fa.base_fwd(q, k, v, causal=w.causal, workspace=ws)  # noqa: E731
-            t_base = min(_timed(base, reps) for _ in range(2))
+            t_base = _graph_timed(base, reps)
             del ws
         pairs = N * (N + 1) / 2 if w.causal else N * N
         fwd_flop = 4.0 * B * H * pairs * d
