@@ -372,8 +372,17 @@ __device__ __forceinline__ void dq_wg(const bf16_t* __restrict__ Q, const bf16_t
   const bool wave_live = qw0 < N;
   const int wave_last_q = min(qw0 + 31, N - 1);
 
+  // The workgroup's Q rows are copied in whole rows into the second tile
+  // pair (idle until the first prefetch) beside the first K and V tiles, and
+  // each wave reads its Q operands from there (loaded straight into
+  // registers, they would be fetched in 32-byte pieces of 32 rows per
+  // instruction); dO rows go straight to registers.
+  static_assert(2 * T::BS == T::B32, "the Q rows fill the second tile pair");
+  bf16_t* const qtile = smem + 2 * T::TILE;
+  int qoff[T::B32 * D / 8 / T::NT];
+  tile_offsets<D, T::B32, T::NT>(qoff, wave, lane);
+  load_tile_async<D, T::B32, T::NT>(qoff, Q + hoff, q0, N, qtile, wave, lane);
   bf16x8 qf[D / 16], dof[D / 16];
-  load_rows_as_b(qf, Q + hoff + (size_t)myq * D, myq < N, hi, D / 16);
   load_rows_as_b(dof, dO + hoff + (size_t)myq * D, myq < N, hi, D / 16);
   const float lse2 = myq < N ? LSE[(size_t)bh * N + myq] * kLog2e : __builtin_huge_valf();
   const float dq_d = myq < N ? Dvec[(size_t)bh * N + myq] : 0.0f;
@@ -435,7 +444,14 @@ __device__ __forceinline__ void dq_wg(const bf16_t* __restrict__ Q, const bf16_t
   wait_vmem_tracked();
   zero_tail<D, T::BS, T::NT>(0, N, ktile(0), wave, lane);
   zero_tail<D, T::BS, T::NT>(0, N, vtile(0), wave, lane);
+  zero_tail<D, T::B32, T::NT>(q0, N, qtile, wave, lane);
   __syncthreads();
+  {
+    const TileReaderX<D> rd = rdx.fresh();
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = rd.row8(qtile, wave, kk);
+  }
+  __syncthreads();  // every wave holds its Q rows: the second tile pair may take K and V
   // One key block: prefetch the next, compute, then wait for the prefetch.
   auto step = [&](int j, auto masked) {
     const int slot = j & 1;
