@@ -87,8 +87,12 @@ def test_ulp_helpers():
 
 
 def test_fl32_is_float32_rounding():
-    x = np.array([1.0 + 2.0 ** -30, 1.0 / 3.0, 1e-45, 3.5e38])
-    assert np.array_equal(B.fl32(x), x.astype(np.float32).astype(np.float64))
+    # hand-derived: 1 + 2^-30 is below half an ulp of 1; 1/3 rounds to
+    # 11184811 * 2^-25; 1e-45 to the smallest subnormal 2^-149; 3.5e38 lies
+    # past the largest finite float32 plus half its ulp, so it overflows
+    x = np.array([1.0 + 2.0 ** -30, 1.0 / 3.0, 1e-45, 3.5e38, -(1.0 + 3 * 2.0 ** -24)])
+    want = [1.0, 11184811 * 2.0 ** -25, 2.0 ** -149, np.inf, -(1.0 + 2.0 ** -22)]
+    assert B.fl32(x).tolist() == want
 
 
 # ---------------------------------------------------------------- shift rule
