@@ -70,6 +70,9 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
 //     v_fma_f32, v_max3_f32, v_med3_f32, v_exp_f32, v_cvt_pk_bf16_f32
 //   kind 6: 8 MFMAs, each followed by 8 v_fma_f32
 //   kind 7: waves 0-3 16 MFMAs, waves 4-7 128 v_fma_f32
+//   kind 12: 8 MFMAs, each followed by 8 v_exp_f32
+//   kind 13: 8 MFMAs, each followed by 8 instructions of the softmax's mix
+//     (2 v_exp_f32, 2 v_fma_f32, 2 v_add_f32, 1 v_max3_f32, 1 v_med3_f32)
 // One float per thread goes to out so that nothing is removed.
 template <int KIND>
 __global__ __launch_bounds__(512, 1) void issue_probe_kernel(float* __restrict__ out, int iters, int active) {
@@ -107,7 +110,14 @@ __global__ __launch_bounds__(512, 1) void issue_probe_kernel(float* __restrict__
     if (KIND == 1 || KIND == 6 || KIND == 7) x[i] = __builtin_fmaf(x[i], m, c);
     if (KIND == 2) x[i] = __builtin_fmaxf(x[i], __builtin_fmaxf(x[(i + 1) & 7], c));
     if (KIND == 3) x[i] = __builtin_amdgcn_fmed3f(x[i], x[(i + 1) & 7], c);
-    if (KIND == 4) x[i] = -exp2_fast(x[i]);
+    if (KIND == 4 || KIND == 12) x[i] = -exp2_fast(x[i]);
+    if (KIND == 13) {
+      if (i < 2) x[i] = -exp2_fast(x[i]);
+      else if (i < 4) x[i] = __builtin_fmaf(x[i], m, c);
+      else if (i < 6) x[i] = x[i] + x[(i + 1) & 7];
+      else if (i == 6) x[i] = __builtin_fmaxf(x[i], __builtin_fmaxf(x[(i + 1) & 7], c));
+      else x[i] = __builtin_amdgcn_fmed3f(x[i], x[(i + 1) & 7], c);
+    }
     if (KIND == 5) {  // one v_cvt_pk_bf16_f32, its packed bits fed back as a float
       typedef __bf16 two_bf16 __attribute__((ext_vector_type(2)));
       two_bf16 r;
@@ -121,7 +131,7 @@ __global__ __launch_bounds__(512, 1) void issue_probe_kernel(float* __restrict__
       for (int it = 0; it < iters; ++it)
 #pragma unroll
         for (int r = 0; r < 8; ++r) acc[r & 3] = mfma<__bf16>(a, b, acc[r & 3]);
-    } else if (KIND == 6) {
+    } else if (KIND == 6 || KIND == 12 || KIND == 13) {
       for (int it = 0; it < iters; ++it) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
@@ -226,7 +236,9 @@ hipError_t launch_issue_probe(int kind, int active, float* out, int blocks, int 
     case 8: hipLaunchKernelGGL(issue_probe_kernel<8>, g, t, 0, s, out, iters, active); break;
     case 9: hipLaunchKernelGGL(issue_probe_kernel<9>, g, t, 0, s, out, iters, active); break;
     case 10: hipLaunchKernelGGL(issue_probe_kernel<10>, g, t, 0, s, out, iters, active); break;
-    default: hipLaunchKernelGGL(issue_probe_kernel<11>, g, t, 0, s, out, iters, active); break;
+    case 11: hipLaunchKernelGGL(issue_probe_kernel<11>, g, t, 0, s, out, iters, active); break;
+    case 12: hipLaunchKernelGGL(issue_probe_kernel<12>, g, t, 0, s, out, iters, active); break;
+    default: hipLaunchKernelGGL(issue_probe_kernel<13>, g, t, 0, s, out, iters, active); break;
   }
   return hipGetLastError();
 }
