@@ -216,30 +216,24 @@ __device__ __forceinline__ void dkdv_wg(const bf16_t* __restrict__ Q, const bf16
   tile_offsets<D, T::BS, T::NT>(ldoff, wave, lane);
 
   // Copies of block qb into stage stg: the Q and dO tiles, and LSE and D of
-  // its rows (wave 0; a block that crosses N takes plain loads and gives the
-  // rows past N LSE = +inf, so that their P and dS vanish).
+  // its rows (LSE by wave 1, D by wave 2, so that no wave carries both on
+  // top of its share of the tiles; a block that crosses N takes plain loads
+  // and gives the rows past N LSE = +inf, so that their P and dS vanish).
+  static_assert(T::NT / 64 >= 3, "waves 1 and 2 copy LSE and D");
   auto issue = [&](int qb, int stg) {
     const int r0 = qb * T::BS;
     load_tile_async<D, T::BS, T::NT>(ldoff, Qh, r0, N, tiles[stg], wave, lane);
     load_tile_async<D, T::BS, T::NT>(ldoff, dOh, r0, N, tiles[stg] + T::TILE, wave, lane);
-    if (wave == 0) {
+    if (wave == 1 || wave == 2) {
+      const float* src = wave == 1 ? LSEh : Dh;
+      float* dst = vecs[stg] + (wave == 1 ? 0 : T::BS);
       if (r0 + T::BS <= N) {
-        if (lane < T::BS / 4)
-          dma16(reinterpret_cast<const bf16_t*>(LSEh + r0), lane * 16u, lds_addr(vecs[stg]));
-        else if (lane < T::BS / 2)
-          dma16(reinterpret_cast<const bf16_t*>(Dh + r0), (lane - T::BS / 4) * 16u, lds_addr(vecs[stg]));
+        if (lane < T::BS / 4) dma16(reinterpret_cast<const bf16_t*>(src + r0), lane * 16u, lds_addr(dst));
       } else if (lane < T::BS) {
         const int q = r0 + lane;
-        vecs[stg][lane] = q < N ? LSEh[q] * kLog2e : __builtin_huge_valf();
-        vecs[stg][T::BS + lane] = q < N ? Dh[q] : 0.0f;
+        dst[lane] = q < N ? src[q] : (wave == 1 ? __builtin_huge_valf() : 0.0f);
       }
     }
-  };
-  // Once wave 0's copies of block qb have landed: LSE -> LSE * log2(e) in
-  // place (the tail path stored it scaled already), so that the elementwise
-  // step takes the base-2 offset straight from LDS.
-  auto scale_lse = [&](int qb, int stg) {
-    if (wave == 0 && lane < T::BS && qb * T::BS + T::BS <= N) vecs[stg][lane] *= kLog2e;
   };
   auto zero_tails = [&](int qb, int stg) {
     zero_tail<D, T::BS, T::NT>(qb * T::BS, N, tiles[stg], wave, lane);
@@ -261,11 +255,11 @@ __device__ __forceinline__ void dkdv_wg(const bf16_t* __restrict__ Q, const bf16
       sacc = mfma<E>(rd.row8(Qs, 0, kk), rd.row8(ktile, wave, kk), sacc);
       dacc = mfma<E>(rd.row8(dOs, 0, kk), vf[kk], dacc);
     }
-    // P = 2^(S c - LSE log2 e); the LDS copy of LSE is pre-scaled
+    // P = 2^(S c - LSE log2 e)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const float4 l4 = *reinterpret_cast<const float4*>(vec + g * 8 + hi * 4);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
 #pragma unroll
       for (int e = 0; e < 4; ++e) sacc[4 * g + e] = exp2_fast(__builtin_fmaf(sacc[4 * g + e], c2, -lv[e]));
     }
@@ -304,7 +298,6 @@ __device__ __forceinline__ void dkdv_wg(const bf16_t* __restrict__ Q, const bf16
   wait_vmem_tracked();
   zero_tail<D, T::B32, T::NT>(k0, N, ktile, wave, lane);
   zero_tails(qb_first, 0);
-  scale_lse(qb_first, 0);
   __syncthreads();
   auto step = [&](int qb, auto masked) {
     const int stg = (qb - qb_first) & 1;
@@ -314,10 +307,7 @@ __device__ __forceinline__ void dkdv_wg(const bf16_t* __restrict__ Q, const bf16
     if (wave_live && !(CAUSAL && qb * T::BS + T::BS - 1 < kw0))
       body(masked, CAUSAL && qb * T::BS < kw0 + 31, qb, stg);
     wait_vmem();
-    if (qb < qb_last) {
-      zero_tails(qb + 1, stg ^ 1);
-      scale_lse(qb + 1, stg ^ 1);
-    }
+    if (qb < qb_last) zero_tails(qb + 1, stg ^ 1);
     __syncthreads();
   };
   // Causal: the blocks that start before the workgroup's last key sit on
