@@ -305,11 +305,13 @@ int fa_hbm_probe(const void* src, size_t bytes, unsigned int* sink, void* stream
  *   bytes per lane (ds_read_b64_tr_b16);  kind 11: 8 MFMAs, each with its A
  *   operand from two transposing LDS reads;  kind 12: 8 MFMAs each followed
  *   by 8 v_exp_f32;  kind 13: 8 MFMAs each followed by 8 instructions of the
- *   softmax's mix (2 exponentials, 2 FMAs, 2 adds, a max3 and a med3).
+ *   softmax's mix (2 exponentials, 2 FMAs, 2 adds, a max3 and a med3);
+ *   kinds 14, 15, 16: 8 MFMAs each followed by 8 v_max3_f32, 8
+ *   v_cvt_pk_bf16_f32 or 8 two-operand v_max_f32.
  * Writes one float per thread to `out` (blocks*512 floats, device memory).
  * Timed with events on `stream`, time / (blocks / CUs) / iters is the time of
  * one iteration of a SIMD's waves.  Returns FA_OK, FA_ERR_INVALID_ARG (kind
- * outside 0..13, waves_per_simd not 1 or 2, kind 7 with one wave, NULL or
+ * outside 0..16, waves_per_simd not 1 or 2, kind 7 with one wave, NULL or
  * misaligned out, non-positive sizes), FA_ERR_DEVICE or FA_ERR_LAUNCH. */
 int fa_issue_probe(int kind, int waves_per_simd, float* out, int blocks, int iters, void* stream);
 

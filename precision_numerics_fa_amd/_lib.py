@@ -469,7 +469,8 @@ def hbm_probe(src, sink=None):
 
 ISSUE_PROBE_KINDS = ("mfma", "v_fma_f32", "v_max3_f32", "v_med3_f32", "v_exp_f32", "v_cvt_pk_bf16_f32",
                      "mfma+fma", "mfma|fma", "ds_read_b128", "mfma(lds a)",
-                     "ds_read_b64_tr_b16", "mfma(lds a, transposing reads)", "mfma+exp", "mfma+softmax mix")
+                     "ds_read_b64_tr_b16", "mfma(lds a, transposing reads)", "mfma+exp", "mfma+softmax mix",
+                     "mfma+max3", "mfma+cvt_pk_bf16", "mfma+max")
 
 
 def issue_probe(kind: int, waves_per_simd: int, blocks: int = 1024, iters: int = 2048, out=None):

@@ -377,7 +377,7 @@ long long fa_mfma_probe(float* out, int blocks, int iters, void* stream) {
 }
 
 int fa_issue_probe(int kind, int waves_per_simd, float* out, int blocks, int iters, void* stream) {
-  if (kind < 0 || kind > 13 || (waves_per_simd != 1 && waves_per_simd != 2) || (kind == 7 && waves_per_simd != 2) ||
+  if (kind < 0 || kind > 16 || (waves_per_simd != 1 && waves_per_simd != 2) || (kind == 7 && waves_per_simd != 2) ||
       out == nullptr || !aligned(out, 4) || blocks < 1 || blocks > (1 << 20) || iters < 1)
     return FA_ERR_INVALID_ARG;
   const int st = check_device();

@@ -73,6 +73,9 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
 //   kind 12: 8 MFMAs, each followed by 8 v_exp_f32
 //   kind 13: 8 MFMAs, each followed by 8 instructions of the softmax's mix
 //     (2 v_exp_f32, 2 v_fma_f32, 2 v_add_f32, 1 v_max3_f32, 1 v_med3_f32)
+//   kind 14: 8 MFMAs, each followed by 8 v_max3_f32
+//   kind 15: 8 MFMAs, each followed by 8 v_cvt_pk_bf16_f32
+//   kind 16: 8 MFMAs, each followed by 8 two-operand v_max_f32
 // One float per thread goes to out so that nothing is removed.
 template <int KIND>
 __global__ __launch_bounds__(512, 1) void issue_probe_kernel(float* __restrict__ out, int iters, int active) {
@@ -108,7 +111,8 @@ __global__ __launch_bounds__(512, 1) void issue_probe_kernel(float* __restrict__
   // (the work of a wave is decided outside its loop, so the loop has no branch)
   auto valu_step = [&](int i) {
     if (KIND == 1 || KIND == 6 || KIND == 7) x[i] = __builtin_fmaf(x[i], m, c);
-    if (KIND == 2) x[i] = __builtin_fmaxf(x[i], __builtin_fmaxf(x[(i + 1) & 7], c));
+    if (KIND == 2 || KIND == 14) x[i] = __builtin_fmaxf(x[i], __builtin_fmaxf(x[(i + 1) & 7], c));
+    if (KIND == 16) x[i] = __builtin_fmaxf(x[i], x[(i + 1) & 7]);
     if (KIND == 3) x[i] = __builtin_amdgcn_fmed3f(x[i], x[(i + 1) & 7], c);
     if (KIND == 4 || KIND == 12) x[i] = -exp2_fast(x[i]);
     if (KIND == 13) {
@@ -118,7 +122,7 @@ __global__ __launch_bounds__(512, 1) void issue_probe_kernel(float* __restrict__
       else if (i == 6) x[i] = __builtin_fmaxf(x[i], __builtin_fmaxf(x[(i + 1) & 7], c));
       else x[i] = __builtin_amdgcn_fmed3f(x[i], x[(i + 1) & 7], c);
     }
-    if (KIND == 5) {  // one v_cvt_pk_bf16_f32, its packed bits fed back as a float
+    if (KIND == 5 || KIND == 15) {  // one v_cvt_pk_bf16_f32, its packed bits fed back as a float
       typedef __bf16 two_bf16 __attribute__((ext_vector_type(2)));
       two_bf16 r;
       r[0] = (__bf16)x[i];
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(512, 1) void issue_probe_kernel(float* __restrict__
       for (int it = 0; it < iters; ++it)
 #pragma unroll
         for (int r = 0; r < 8; ++r) acc[r & 3] = mfma<__bf16>(a, b, acc[r & 3]);
-    } else if (KIND == 6 || KIND == 12 || KIND == 13) {
+    } else if (KIND == 6 || KIND >= 12) {
       for (int it = 0; it < iters; ++it) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
@@ -238,7 +242,10 @@ hipError_t launch_issue_probe(int kind, int active, float* out, int blocks, int 
     case 10: hipLaunchKernelGGL(issue_probe_kernel<10>, g, t, 0, s, out, iters, active); break;
     case 11: hipLaunchKernelGGL(issue_probe_kernel<11>, g, t, 0, s, out, iters, active); break;
     case 12: hipLaunchKernelGGL(issue_probe_kernel<12>, g, t, 0, s, out, iters, active); break;
-    default: hipLaunchKernelGGL(issue_probe_kernel<13>, g, t, 0, s, out, iters, active); break;
+    case 13: hipLaunchKernelGGL(issue_probe_kernel<13>, g, t, 0, s, out, iters, active); break;
+    case 14: hipLaunchKernelGGL(issue_probe_kernel<14>, g, t, 0, s, out, iters, active); break;
+    case 15: hipLaunchKernelGGL(issue_probe_kernel<15>, g, t, 0, s, out, iters, active); break;
+    default: hipLaunchKernelGGL(issue_probe_kernel<16>, g, t, 0, s, out, iters, active); break;
   }
   return hipGetLastError();
 }

@@ -175,8 +175,8 @@ def test_probe_argument_validation(lib):
     assert lib.fa_hbm_probe(GOOD, 100, P(1 << 20), None) == -1         # not a multiple of 16
     assert lib.fa_hbm_probe(GOOD, 256, None, None) == -1               # no sink
     assert lib.fa_hbm_probe(P(4100), 256, P(1 << 20), None) == -1      # misaligned
-    assert lib.fa_issue_probe(-1, 1, GOOD, 4, 4, None) == -1           # kind outside 0..13
-    assert lib.fa_issue_probe(14, 1, GOOD, 4, 4, None) == -1
+    assert lib.fa_issue_probe(-1, 1, GOOD, 4, 4, None) == -1           # kind outside 0..16
+    assert lib.fa_issue_probe(17, 1, GOOD, 4, 4, None) == -1
     assert lib.fa_issue_probe(0, 3, GOOD, 4, 4, None) == -1            # one or two waves per SIMD
     assert lib.fa_issue_probe(7, 1, GOOD, 4, 4, None) == -1            # kind 7 pairs two waves
     assert lib.fa_issue_probe(0, 1, None, 4, 4, None) == -1
