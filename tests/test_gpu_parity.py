@@ -273,6 +273,29 @@ def test_c2_full_and_tie_bias(fa):
     assert abs(res[True][0]) < 0.5 * res[False][0]
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_long_noncausal_forward_backward(fa, d):
+    """Without the causal mask at N = 4096 every workgroup runs all 32 key
+    blocks (forward) and every dK/dV and dQ workgroup all of its head's
+    blocks, through the steady paths the masked runs leave early: O, LSE and
+    the gradients of two heads against the exact oracle."""
+    B, H, N = 1, 2, 4096
+    scale = d ** -0.5
+    say(f"non-causal {B}x{H}x{N}x{d} forward+backward")
+    bits, dev = random_case(B, H, N, d, seed=91 + d, with_do=True)
+    o, lse = fa.fwd(dev["q"], dev["k"], dev["v"], causal=False, stabilize=True)
+    dq, dk, dv = fa.bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=False)
+    for h in range(H):
+        q, k, v, do = (head_f64(bits[n][0, h]) for n in ("q", "k", "v", "do"))
+        o_ref, lse_ref = REF.forward(q, k, v, scale, False)
+        _gate_o(to_f64(o[0, h]), o_ref)
+        assert lse_err(lse[0, h].cpu().numpy(), lse_ref) <= LSE_TOL
+        rq, rk, rv = REF.backward(q, k, v, do, scale, False)
+        for name, g, r in (("dq", dq[0, h], rq), ("dk", dk[0, h], rk), ("dv", dv[0, h], rv)):
+            rel = Mt.relative_fro(to_f64(g), r)
+            assert rel <= GRAD_REL, (name, h, rel)
+
+
 @pytest.mark.parametrize("stabilize", [False, True])
 def test_c3_full_sampled_heads(fa, stabilize):
     w = F.WORKLOADS["c3"]
