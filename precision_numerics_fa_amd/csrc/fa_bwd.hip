@@ -532,7 +532,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grads_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
     bf16_t* __restrict__ dQ, bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int N, int n_blk,
-    int total_blocks, int xcd_remap, float c2, float scale, int BH, int G, int block_major) {
+    int total_blocks, int xcd_remap, float c2, float scale, int BH, int G, int chunk) {
   constexpr int B0 = DkdvTile<D>::LDS_BYTES, B1 = DqTile<D>::LDS_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char lds[B0 > B1 ? B0 : B1];
   const int bid = logical_block(total_blocks, xcd_remap);
@@ -543,11 +543,16 @@ __global__ __launch_bounds__(256, 2) void bwd_grads_kernel(
   const int r = bid - g * per_group;
   const bool is_dq = r >= G * n_blk;
   const int r2 = is_dq ? r - G * n_blk : r;
-  // head-major (a head's blocks together: its tensors stay in L2), or, for
-  // small launches, block-major (every head's heaviest block first: the
-  // longest workgroups start first)
-  const int bh = g * G + (block_major ? r2 % G : r2 / n_blk);
-  const int blk = block_major ? r2 / G : r2 % n_blk;
+  // Within each kind the group's heads go in chunks of `chunk` heads (chunk
+  // divides G), one chunk after the other, block-major within a chunk
+  // (every head's heaviest block first).  chunk = 1 is head-major (a head's
+  // blocks together: its tensors stay in L2), chunk = G block-major over the
+  // group (the longest workgroups start first).
+  const int per_chunk = chunk * n_blk;
+  const int ck = r2 / per_chunk;
+  const int cw = r2 - ck * per_chunk;
+  const int bh = g * G + ck * chunk + cw % chunk;
+  const int blk = cw / chunk;
   if (bh >= BH) return;
   if (is_dq)
     dq_wg<E, D, CAUSAL>(Q, K, V, dO, LSE, Dvec, dQ, N, c2, scale, bh, n_blk - 1 - blk, lds);
@@ -602,12 +607,19 @@ hipError_t launch_grads_t(const BwdArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;
   const int G = (BH + 7) / 8;  // heads per group: one group per XCD
   const long long total = (long long)((BH + G - 1) / G) * 2 * G * n_blk;
-  // a launch of a few rounds of workgroups is bound by its longest ones
-  const int block_major = total <= kGradsBlockMajorMax ? 1 : 0;
+  // A launch of a few rounds of workgroups is bound by its longest ones
+  // (block-major); longer causal launches go in chunks of four heads, so that
+  // the last heads' heaviest workgroups do not start at the very end (bitwise
+  // the same gradients; 4x32x4096x128 1.885 -> 1.808 ms, 16x32x1024x128
+  // 0.664 -> 0.609, 64x16x2048x64 2.209 -> 2.090, 2x16x8192x128 -1%; chunks
+  // of two and eight gave 1.851 and 1.827 at the first); without the mask
+  // every workgroup of a kind costs the same and the order stays head-major.
+  const int chunk =
+      total <= kGradsBlockMajorMax ? G : (CAUSAL ? (G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1)) : 1);
   hipLaunchKernelGGL((bwd_grads_kernel<E, D, CAUSAL>), dim3((unsigned)total), dim3(256), 0, s,
                      (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.dout,
                      a.lse, a.dvec, (bf16_t*)a.dq, (bf16_t*)a.dk, (bf16_t*)a.dv, a.N, n_blk, (int)total,
-                     remap_ok(total), scale_log2e(a.scale), a.scale, BH, G, block_major);
+                     remap_ok(total), scale_log2e(a.scale), a.scale, BH, G, chunk);
   return hipGetLastError();
 }
 
