@@ -536,11 +536,15 @@ __global__ __launch_bounds__(256, FwdTile<D>::SEQ ? 3 : 2) void fwd_kernel(
   }
 }
 
-// Up to this many workgroups (four per CU) the forward orders each XCD
-// group's query blocks block-major (see fwd_kernel).  Measured, causal:
-// N=1024 d=64 with 768 and 2048 workgroups 39.1 -> 28.7 us and 82.4 ->
-// 61.2 us; N=4096 d=128 (4096 workgroups) is no faster block-major.
-constexpr long long kFwdBlockMajorMax = 2048;
+// Launches of up to 5.5 rounds of resident workgroups (two per CU at
+// d = 128, three at d = 64, 256 CUs) order each XCD group's query blocks
+// block-major (see fwd_kernel).  Measured, causal: N=1024 d=64 with 768 and
+// 2048 workgroups 39.1 -> 28.7 us and 82.4 -> 61.2 us, and with 4096
+// workgroups (5.3 rounds) 0.129 -> 0.117 ms against chunks of four heads;
+// N=4096 and N=1024 d=128 with 4096 workgroups (8 rounds) 0.569 -> 0.596 ms
+// and 0.213 -> 0.224 ms, slower block-major than in chunks of four; with 2560
+// workgroups (5 rounds, 2x40x4096x128) 0.385 -> 0.367 ms block-major.
+constexpr long long kFwdBlockMajorHalfRounds = 11;
 
 template <typename E, int D, bool CAUSAL, bool STAB, bool DIAG>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
@@ -556,7 +560,10 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   // same outputs): 4x32x4096x128 0.600 -> 0.575 ms, 16x32x1024x128 0.238 ->
   // 0.209 ms, 2x16x8192x128 unchanged; without the causal mask, where every
   // block costs the same, chunks of four were 1% slower.
-  const int chunk = total <= kFwdBlockMajorMax ? G : (CAUSAL ? (G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1)) : 1);
+  constexpr long long resident = 256LL * (FwdTile<D>::SEQ ? 3 : 2);
+  const int chunk = 2 * total <= kFwdBlockMajorHalfRounds * resident
+                        ? G
+                        : (CAUSAL ? (G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1)) : 1);
   hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, STAB, DIAG, false>), dim3((unsigned)total), dim3(256), 0, stream,
                      (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (bf16_t*)a.o, a.lse,
                      a.row_shifted, a.N, n_qblk, (int)total, remap, scale_log2e(a.scale), BH, G, chunk,
