@@ -536,19 +536,30 @@ __global__ __launch_bounds__(256, 2) void bwd_grads_kernel(
   constexpr int B0 = DkdvTile<D>::LDS_BYTES, B1 = DqTile<D>::LDS_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char lds[B0 > B1 ? B0 : B1];
   const int bid = logical_block(total_blocks, xcd_remap);
-  // heads in groups of G (one group per XCD): a group's dK/dV workgroups
-  // first, then its dQ workgroups
+  // Heads in groups of G (one group per XCD), a group's heads in chunks of
+  // `chunk` heads (chunk divides G), one chunk after the other, block-major
+  // within a chunk (every head's heaviest block first).  chunk = 1 is
+  // head-major (a head's blocks together: its tensors stay in L2), chunk = G
+  // block-major over the group (the longest workgroups start first).  With
+  // chunk = 1 or G a group's dK/dV workgroups come first, then its dQ
+  // workgroups; with chunks in between each chunk's dK/dV workgroups are
+  // followed by its own dQ workgroups, which find the chunk's tensors still
+  // in L2.
   const int per_group = 2 * G * n_blk;
   const int g = bid / per_group;
   const int r = bid - g * per_group;
-  const bool is_dq = r >= G * n_blk;
-  const int r2 = is_dq ? r - G * n_blk : r;
-  // Within each kind the group's heads go in chunks of `chunk` heads (chunk
-  // divides G), one chunk after the other, block-major within a chunk
-  // (every head's heaviest block first).  chunk = 1 is head-major (a head's
-  // blocks together: its tensors stay in L2), chunk = G block-major over the
-  // group (the longest workgroups start first).
   const int per_chunk = chunk * n_blk;
+  bool is_dq;
+  int r2;
+  if (chunk > 1 && chunk < G) {
+    const int c = r / (2 * per_chunk);
+    const int w = r - c * 2 * per_chunk;
+    is_dq = w >= per_chunk;
+    r2 = c * per_chunk + (is_dq ? w - per_chunk : w);
+  } else {
+    is_dq = r >= G * n_blk;
+    r2 = is_dq ? r - G * n_blk : r;
+  }
   const int ck = r2 / per_chunk;
   const int cw = r2 - ck * per_chunk;
   const int bh = g * G + ck * chunk + cw % chunk;
@@ -612,8 +623,10 @@ hipError_t launch_grads_t(const BwdArgs& a, hipStream_t s) {
   // the last heads' heaviest workgroups do not start at the very end (bitwise
   // the same gradients; 4x32x4096x128 1.885 -> 1.808 ms, 16x32x1024x128
   // 0.664 -> 0.609, 64x16x2048x64 2.209 -> 2.090, 2x16x8192x128 -1%; chunks
-  // of two and eight gave 1.851 and 1.827 at the first); without the mask
-  // every workgroup of a kind costs the same and the order stays head-major.
+  // of two and eight gave 1.851 and 1.827 at the first), each chunk's dQ
+  // workgroups right after its dK/dV ones (a further 1.746 -> 1.715 ms,
+  // 0.581 -> 0.556, 2.015 -> 1.963); without the mask every workgroup of a
+  // kind costs the same and the order stays head-major.
   const int chunk =
       total <= kGradsBlockMajorMax ? G : (CAUSAL ? (G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1)) : 1);
   hipLaunchKernelGGL((bwd_grads_kernel<E, D, CAUSAL>), dim3((unsigned)total), dim3(256), 0, s,
