@@ -605,11 +605,15 @@ hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Up to this many workgroups (eight per CU), the dQ/dK/dV launch orders each
-// XCD group's blocks block-major.  Measured: N=1024 d=64 with 4096
-// workgroups 0.175 -> 0.157 ms; at N=2048 d=64 (32768 workgroups) the
-// block-major order is 9% slower (its heads no longer share L2).
-constexpr long long kGradsBlockMajorMax = 4096;
+// Launches of up to 5.5 rounds of resident workgroups (two per CU at
+// d = 128, three at d = 64, 256 CUs), the dQ/dK/dV launch orders each XCD
+// group's blocks block-major.  Measured: N=1024 d=64 with 4096 workgroups
+// (5.3 rounds) 0.175 -> 0.157 ms against head-major, and 0.155 -> 0.149 ms
+// against chunks of four heads; N=1024 d=128 with 4096 workgroups (8
+// rounds) 0.3056 -> 0.2985 ms (median) in chunks of four instead; at N=2048
+// d=64 (32768 workgroups) block-major is 9% slower than head-major (its
+// heads no longer share L2).
+constexpr long long kGradsBlockMajorHalfRounds = 11;
 
 template <typename E, int D, bool CAUSAL>
 hipError_t launch_grads_t(const BwdArgs& a, hipStream_t s) {
@@ -628,7 +632,9 @@ hipError_t launch_grads_t(const BwdArgs& a, hipStream_t s) {
   // 0.581 -> 0.556, 2.015 -> 1.963); without the mask every workgroup of a
   // kind costs the same and the order stays head-major.
   const int chunk =
-      total <= kGradsBlockMajorMax ? G : (CAUSAL ? (G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1)) : 1);
+      2 * total <= kGradsBlockMajorHalfRounds * 256LL * (D == 64 ? 3 : 2)
+          ? G
+          : (CAUSAL ? (G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1)) : 1);
   hipLaunchKernelGGL((bwd_grads_kernel<E, D, CAUSAL>), dim3((unsigned)total), dim3(256), 0, s,
                      (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.dout,
                      a.lse, a.dvec, (bf16_t*)a.dq, (bf16_t*)a.dk, (bf16_t*)a.dv, a.N, n_blk, (int)total,
