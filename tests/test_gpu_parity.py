@@ -296,6 +296,64 @@ def test_long_noncausal_forward_backward(fa, d):
             assert rel <= GRAD_REL, (name, h, rel)
 
 
+def _order_chunk(BH, n_blk, per_head, d, causal=True):
+    """Heads per chunk that a launch of BH heads with n_blk blocks each (per
+    kind) takes: every head of an XCD group block-major (G) up to 5.5 rounds
+    of resident workgroups (two per CU at d = 128, three at d = 64), else
+    chunks of four, two or one heads by what divides the group's head count G
+    (causal; head-major without the mask).  per_head: 1 (forward), 2 (the
+    dQ/dK/dV launch, both kinds)."""
+    G = (BH + 7) // 8
+    total = -(-BH // G) * G * per_head * n_blk
+    if 2 * total <= 11 * 256 * (3 if d == 64 else 2):
+        return G
+    return (4 if G % 4 == 0 else 2 if G % 2 == 0 else 1) if causal else 1
+
+
+# causal shapes whose long launches take chunks of two heads (G = 6 with four
+# padding heads, G = 14) and of one head (G = 5, G = 25)
+ORDER_SHAPES = [(128, 4, 11, 7680, 2), (128, 1, 40, 9216, 1), (64, 1, 112, 4864, 2), (64, 8, 25, 3072, 1)]
+
+
+@pytest.mark.parametrize("d,B,H,N,chunk", ORDER_SHAPES)
+def test_chunked_launch_orders_cover_every_head(fa, d, B, H, N, chunk):
+    """The forward and the dQ/dK/dV launch of a long causal launch walk an
+    XCD group's heads in chunks whose size depends on the group's head count.
+    Each workgroup's result does not depend on where the order puts it, so
+    every head's O, LSE and gradients must equal, bit for bit, those of
+    launches of at most eight heads (a single head per group); a workgroup
+    the order skipped or ran twice would leave some head's rows unwritten.
+    The last head (the last chunk of the last group) is also checked against
+    the exact oracle."""
+    import torch
+    raw = lambda t: t.view(torch.int32 if t.dtype == torch.float32 else torch.int16)
+    BH, n_blk = B * H, -(-N // 128)
+    assert _order_chunk(BH, n_blk, 1, d) == chunk and _order_chunk(BH, n_blk, 2, d) == chunk
+    scale = d ** -0.5
+    say(f"launch order, chunks of {chunk}: causal {B}x{H}x{N}x{d}")
+    bits, dev = random_case(B, H, N, d, seed=700 + d + H, with_do=True)
+    o, lse = fa.fwd(dev["q"], dev["k"], dev["v"], causal=True, stabilize=True)
+    dq, dk, dv = fa.bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=True)
+    for b in range(B):
+        for h0 in range(0, H, 8):
+            sl = lambda t: t[b:b + 1, h0:h0 + 8].contiguous()  # noqa: E731
+            q, k, v, do = (sl(dev[n]) for n in ("q", "k", "v", "do"))
+            o8, lse8 = fa.fwd(q, k, v, causal=True, stabilize=True)
+            g8 = fa.bwd(q, k, v, o8, do, lse8, causal=True)
+            for name, big, small in (("o", o, o8), ("lse", lse, lse8), ("dq", dq, g8[0]), ("dk", dk, g8[1]),
+                                     ("dv", dv, g8[2])):
+                assert torch.equal(raw(sl(big)), raw(small)), (name, b, h0)
+    b, h = B - 1, H - 1
+    q, k, v, do = (head_f64(bits[n][b, h]) for n in ("q", "k", "v", "do"))
+    o_ref, lse_ref = REF.forward(q, k, v, scale, True)
+    _gate_o(to_f64(o[b, h]), o_ref)
+    assert lse_err(lse[b, h].cpu().numpy(), lse_ref) <= LSE_TOL
+    rq, rk, rv = REF.backward(q, k, v, do, scale, True)
+    for name, g, r in (("dq", dq[b, h], rq), ("dk", dk[b, h], rk), ("dv", dv[b, h], rv)):
+        rel = Mt.relative_fro(to_f64(g), r)
+        assert rel <= GRAD_REL, (name, h, rel)
+
+
 @pytest.mark.parametrize("stabilize", [False, True])
 def test_c3_full_sampled_heads(fa, stabilize):
     w = F.WORKLOADS["c3"]
